@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of one key-eviction pass (score + top-B select + compaction) on one MI355X.
+
+A step is one pass over the Qwen3-8B-shaped layer workload (8 KV heads x 32768 bf16 keys,
+d = 128, theta = 1e6, offsets 2^0..2^16, B = 2048): tri_score (with the fused radix
+histogram), tri_select_topb and tri_compact_kv, all on the current stream. Inputs are resident
+in HBM; to keep the 256 MB Infinity Cache from serving them, consecutive steps rotate over
+``--rotate`` distinct copies of the inputs and outputs (about 135 MB per copy).
+
+Prints ONE JSON line (rank 0). Extra legs:
+  --pmc-copy       only run a plain device copy of known size (for counter calibration)
+  --no-cpu         skip the CPU baseline
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E spec
+METRIC = "cached keys scored+selected/sec and achieved HBM GB/s (% of peak), 32k keys"
+
+
+def algorithmic_bytes(wl, n_keys_total, n_units):
+    """Bytes the method must move per pass: every K row and position read, the kept V rows
+    read, the kept K/V rows and positions written."""
+    e = wl.elem_bytes
+    B = wl.budget
+    return {
+        "K": n_keys_total * wl.d * e,
+        "pos": n_keys_total * 4,
+        "V_kept": n_units * B * wl.d * e,
+        "writes": n_units * B * (2 * wl.d * e + 4),
+    }
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ["tri_kernels.hip", "tri_internal.h"]:
+        with open(os.path.join(ROOT, "rotary_frequency_key_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_hash):
+    """HBM traffic per score launch from the committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "score_kernel_c2_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel source sha256\[:16\]:\s*([0-9a-f]+)", txt)
+    m_val = re.search(r"traffic bytes per launch \(scaled\):\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_hash:
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(wl, P, budget, seconds_target=10.0):
+    """The fp64 oracle (folded score + select + gather), unchanged, over the units of the
+    workload, one process per unit up to the host cores; repeated until ~seconds_target."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    units = list(range(len(P["row_off"]) - 1))
+    cores = max(1, min(len(units), len(os.sched_getaffinity(0)), 16))
+    jobs = []
+    for i in units:
+        a, b = P["row_off"][i], P["row_off"][i + 1]
+        jobs.append((P["centers"][i], P["keys"][a:b], P["values"][a:b], P["pos"][a:b],
+                     int(P["t"][i]), wl.d, wl.theta, budget))
+    passes = 0
+    keys = 0
+    with ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_oracle_job, jobs[:cores]))  # start the workers
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(_oracle_job, jobs))
+            passes += 1
+            keys += int(P["row_off"][-1])
+            if time.perf_counter() - t0 >= seconds_target or passes >= 50:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": keys / dt, "unit": "keys/s", "cores": cores, "kind": "oracle",
+            "sample": f"{passes} full passes over all {len(units)} units ({keys} keys) of the same "
+                      f"workload, fp64 NumPy folded score + select + gather, {dt:.1f} s"}
+
+
+def _oracle_job(args):
+    import oracle as O
+
+    center, keys, values, pos, t, d, theta, budget = args
+    O.unit_pass(center, keys, values, pos, t, d, theta, O.power_of_two_offsets(), budget)
+    return 0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--pmc-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: every unit is scored, selected and compacted "
+              "independently, so more GPUs would each run this same pass on their own units. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rotary_frequency_key_amd as tri
+    from synthgen import pack_units, workload
+
+    dev = torch.device("cuda:0")
+
+    if args.pmc_copy:
+        # plain device copy of a known size for FETCH_SIZE / WRITE_SIZE calibration
+        n = 256 << 20
+        a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return
+
+    wl = workload("c2")
+    P = pack_units(wl, workers=min(8, len(os.sched_getaffinity(0))))
+    U = wl.n_units
+    R = int(P["row_off"][-1])
+    B = wl.budget
+    max_rows = int(np.diff(P["row_off"]).max())
+    _, mu = tri.tri_fold_weights(wl.d, wl.theta, np.array([1 << j for j in range(17)]), P["centers"])
+
+    def dev_bf16(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    copies = []
+    for _ in range(args.rotate):
+        c = {
+            "K": dev_bf16(P["keys"]),
+            "V": dev_bf16(P["values"]),
+            "pos": torch.from_numpy(P["pos"]).to(dev),
+            "row_off": torch.from_numpy(P["row_off"]).to(dev),
+            "t": torch.from_numpy(P["t"]).to(dev),
+            "mu": torch.from_numpy(mu).to(dev),
+            "ws": tri.make_workspace(U, dev),
+            "scores": torch.empty(R, dtype=torch.float32, device=dev),
+            "kept_idx": torch.empty((U, B), dtype=torch.int32, device=dev),
+            "kept_cnt": torch.empty(U, dtype=torch.int32, device=dev),
+            "K_out": torch.empty((U, B, wl.d), dtype=torch.bfloat16, device=dev),
+            "V_out": torch.empty((U, B, wl.d), dtype=torch.bfloat16, device=dev),
+            "pos_out": torch.empty((U, B), dtype=torch.int32, device=dev),
+        }
+        c["plan"] = tri.PassPlan(c["K"], c["V"], c["pos"], c["row_off"], max_rows, c["t"], c["mu"],
+                                 wl.theta, B, ws=c["ws"], scores=c["scores"], kept_idx=c["kept_idx"],
+                                 kept_cnt=c["kept_cnt"], K_out=c["K_out"], V_out=c["V_out"],
+                                 pos_out=c["pos_out"])
+        copies.append(c)
+    plans = [c["plan"] for c in copies]
+
+    def step(i, ev=None):
+        plan = plans[i % len(plans)]
+        if ev is None:
+            plan.run()
+            return
+        ev[0].record()
+        plan.score()
+        ev[1].record()
+        plan.select()
+        ev[2].record()
+        plan.compact()
+        ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K whole passes
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} passes: {ms * 1e3:.2f} us/pass (host wall {t_wall / args.steps * 1e6:.2f} us)",
+          file=sys.stderr, flush=True)
+
+    # per-kernel durations: HIP events bracket each launch on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    k_score = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    k_select = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    k_compact = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+
+    alg = algorithmic_bytes(wl, R, U)
+    alg_total = sum(alg.values())
+    secs = ms * 1e-3
+    keys_per_s = R / secs
+    gbps = alg_total / secs / 1e9
+    score_bytes = alg["K"] + alg["pos"]
+    score_gbps = score_bytes / (k_score * 1e-6) / 1e9
+    khash = kernel_source_hash()
+    traffic = read_traffic(khash)
+
+    result = {
+        "metric": METRIC,
+        "value": keys_per_s,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-8B-shaped layer: 8 KV heads x 32768 keys, d=128, bf16 K/V, "
+                        "theta=1e6, D=2^0..2^16, B=2048",
+            "units": U, "keys_per_unit": max_rows, "d": wl.d, "kv_dtype": "bf16",
+            "budget": B, "theta": wl.theta,
+            "cold_cache": f"{args.rotate} rotating input/output copies",
+        },
+        "hbm_gbps": gbps,
+        "hbm_frac_of_peak": gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_pass": alg_total,
+        "kernels_us": {"score": k_score, "select": k_select, "compact": k_compact},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "score_kernel<bf16, interleaved, 128, hist>",
+            "achieved": score_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": score_gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": score_bytes,
+        },
+        "kernel_source_sha256_16": khash,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl, P, B, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

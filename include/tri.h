@@ -1,0 +1,197 @@
+/*
+ * tri.h - C interface of libtri: the key-eviction pass of TriAttention on MI355X (gfx950).
+ *
+ * One pass over a KV cache made of independent *units* (one KV head of one layer of one
+ * sequence) does three things:
+ *   1. scores every cached key with the offset-averaged trigonometric score, folded into
+ *      one complex weight per rotary band;
+ *   2. keeps the B highest-scoring keys of each unit;
+ *   3. copies the kept K/V rows and positions into dense per-unit buffers.
+ *
+ * Sources (cited by title and section):
+ *   [N] "The future-offset average in TriAttention can be precomputed" (A. Mukherjee):
+ *       "The score TriAttention computes", "The same score, read as arrows in the plane",
+ *       "The averaging step", "What it saves, and what it does not".
+ *   [R] TriAttention project README: KV budget settings for serving and chat.
+ *
+ * Notation: d = head dimension (even), F = d/2 rotary bands, U = units, N_u = cached keys of
+ * unit u, B = budget (rows kept per unit), t_u = current position of unit u, p = a key's
+ * position, delta = t_u - p. Band f of a d-vector x is the complex number x[2f] + i*x[2f+1]
+ * ("interleaved" pairs). omega_f = theta^(-2f/d) ([N] "The score TriAttention computes").
+ *
+ * Conventions shared by every entry point:
+ *  - Return value: TRI_OK (0) or a negative TRI_ERR_* code. Nothing throws across the ABI.
+ *  - All argument checks run on the host before any HIP call; when a check fails nothing is
+ *    enqueued and no output is touched.
+ *  - The caller owns every buffer. The library allocates no device memory and keeps no state
+ *    between calls, except what a caller-provided workspace holds (tri_score/tri_select_topb).
+ *  - Device entry points are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream). Nothing synchronises the host.
+ *  - Device pointers must be 16-byte aligned unless stated otherwise.
+ *  - Device-side preconditions that the host cannot check (row_off contents, positions) are
+ *    stated per function. Kernels clamp every row range to [0, total_rows), so a broken
+ *    row_off yields wrong values, never an access outside the buffers.
+ */
+#ifndef TRI_H
+#define TRI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TRI_OK               0
+#define TRI_ERR_ARG         -1  /* bad size, pointer, alignment or enum value */
+#define TRI_ERR_UNSUPPORTED -2  /* valid request that this build does not implement */
+#define TRI_ERR_ALIAS       -3  /* an output range overlaps an input range or another output */
+#define TRI_ERR_WORKSPACE   -4  /* workspace missing or smaller than required */
+#define TRI_ERR_HIP         -5  /* the HIP runtime reported an error at launch */
+
+/* element types of K and V */
+#define TRI_DT_F32  0  /* IEEE binary32 */
+#define TRI_DT_BF16 1  /* bfloat16 (upper half of a binary32) */
+
+/* how the d coordinates of a key pair up into F complex bands */
+#define TRI_BANDS_INTERLEAVED 0  /* band f = (x[2f], x[2f+1]) */
+#define TRI_BANDS_HALF_SPLIT  1  /* band f = (x[f], x[f + d/2]) (rotate-half storage) */
+
+/* flags of tri_select_topb */
+#define TRI_SELECT_HIST_FROM_SCORE 1u  /* ws holds the histogram tri_score accumulated */
+
+/* Short English text for a status code (static storage; never NULL). */
+const char* tri_status_string(int status);
+
+/*
+ * tri_fold_weights - offline fold of the offset schedule into one weight per band.
+ *
+ *   W_f    = (1/|D|) * sum_{delta in D} e^{i omega_f delta}                 (f = 0 .. F-1)
+ *   mu'_f  = E[q_f] * W_f                        per unit, the offset-averaged center
+ *
+ * [N] "The averaging step": the average over future offsets touches only the rotation
+ * factor e^{i omega_f delta}, so it collapses into W_f, computed once, offline, alongside the
+ * centers; the averaged score is one evaluation with the center replaced by mu'.
+ *
+ * Host function, fp64, synchronous; touches no GPU.
+ *   d          head dimension: even, 2 <= d <= 512
+ *   theta      rotary base (> 0, finite)
+ *   offsets    host int64[n_offsets], the schedule D (e.g. 1, 2, 4, ..., 65536); any values
+ *   n_offsets  >= 1
+ *   centers    host float[n_units][F][2]: E[q_f] as (re, im), or NULL (then mu_out is not
+ *              written and n_units is ignored)
+ *   n_units    >= 0
+ *   W_out      host double[F][2] (re, im): always written
+ *   mu_out     host float[n_units][F][2]: mu' rounded once from fp64 to binary32 (nearest);
+ *              may be NULL; written only when centers != NULL
+ * Errors: TRI_ERR_ARG for a bad size, theta, or a NULL W_out / offsets.
+ */
+int tri_fold_weights(int d, double theta, const int64_t* offsets, int n_offsets,
+                     const float* centers, int n_units, double* W_out, float* mu_out);
+
+/*
+ * tri_score - offset-averaged trigonometric score of every cached key.
+ *
+ *   score[r] = Re{ sum_f mu'_{u,f} * conj(k_{r,f}) * e^{i omega_f (t_u - pos[r])} }
+ *
+ * for every row r of unit u. [N] "The same score, read as arrows in the plane" (complex
+ * form of the rotary score) and "The averaging step" (the same form with mu' = E[q] W
+ * equals the average over the offset schedule). The norm term S_norm of [N] "The score
+ * TriAttention computes" is not defined there and is not included.
+ *
+ *   keys        device, [total_rows][d] elements of `dtype`, rows of unit u at
+ *               row_off[u] .. row_off[u+1]-1
+ *   dtype       TRI_DT_BF16 or TRI_DT_F32
+ *   layout      TRI_BANDS_INTERLEAVED or TRI_BANDS_HALF_SPLIT
+ *   d           64, 128 or 256
+ *   theta       rotary base (> 0, finite); the kernel derives omega_f from it
+ *   row_off     device int64[n_units+1]: 0 = row_off[0] <= row_off[1] <= ... = total_rows
+ *   n_units     >= 1
+ *   total_rows  host copy of row_off[n_units] (>= 0)
+ *   max_rows    host bound on every N_u (>= 0); rows of a unit beyond it are not scored
+ *   pos         device int32[total_rows]: position of each key
+ *   t_now       device int32[n_units]: current position of each unit
+ *   mu          device float[n_units][F][2]: mu' (tri_fold_weights' mu_out)
+ *   scores      device float[total_rows]: output (binary32); must not overlap the inputs
+ *   ws          device workspace or NULL; see below
+ *   ws_bytes    in/out, see below
+ *   stream      hipStream_t or NULL
+ * Workspace protocol (optional radix histogram for tri_select_topb):
+ *   ws_bytes == NULL             no workspace: scores only.
+ *   ws == NULL, ws_bytes != NULL  query: *ws_bytes = required size; returns TRI_OK, no launch.
+ *   both non-NULL                 *ws_bytes must be >= the required size (else
+ *                                 TRI_ERR_WORKSPACE). The workspace must be in its rest state
+ *                                 (all zero: zero-fill it once after allocation); the score
+ *                                 kernel adds each unit's 12-bit top-digit histogram of the
+ *                                 scores into it, and tri_select_topb called with
+ *                                 TRI_SELECT_HIST_FROM_SCORE and the same ws consumes it and
+ *                                 returns ws to its rest state.
+ * Device preconditions: 0 <= t_u - pos[r] < 2^24; finite keys and mu'.
+ * Precision: rotation phase in 23-bit fixed point plus a binary32 residual, hardware
+ *   sine/cosine, binary32 accumulation; mu' enters as a two-term bfloat16 split for bf16 keys.
+ */
+int tri_score(const void* keys, int dtype, int layout, int d, double theta,
+              const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
+              const int32_t* pos, const int32_t* t_now, const float* mu, float* scores,
+              void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * tri_select_topb - keep the B highest-scoring rows of each unit.
+ *
+ * [N] introduction: when the cache must be trimmed, every key is scored and the
+ * highest-scoring ones are kept. [R] chat settings: a KV budget (default 2048, 12000 for
+ * chat) bounds the cache. Order: score descending; equal scores keep the lower row index;
+ * -0.0 equals +0.0; NaN ranks below every number. Exactly min(B, N_u) rows are kept.
+ *
+ *   scores    device float[total_rows]
+ *   row_off   device int64[n_units+1] (as in tri_score)
+ *   n_units   >= 1
+ *   total_rows host copy of row_off[n_units]
+ *   max_rows  host bound on every N_u; must be < 2^31
+ *   B         budget per unit, 0 <= B < 2^31
+ *   kept_idx  device int32[n_units][B]: the kept rows' local indices (0 .. N_u-1) in
+ *             ascending order, then -1 up to B
+ *   kept_cnt  device int32[n_units]: min(B, N_u)
+ *   ws, ws_bytes  workspace, same protocol as tri_score. Without
+ *             TRI_SELECT_HIST_FROM_SCORE the histogram is computed here (ws may be NULL with
+ *             ws_bytes NULL). With it, ws must be the workspace tri_score just filled for
+ *             these scores and row_off; on return it is back in its rest state.
+ *   flags     0 or TRI_SELECT_HIST_FROM_SCORE
+ *   stream    hipStream_t or NULL
+ */
+int tri_select_topb(const float* scores, const int64_t* row_off, int n_units,
+                    int64_t total_rows, int64_t max_rows, int B, int32_t* kept_idx,
+                    int32_t* kept_cnt, void* ws, size_t* ws_bytes, unsigned flags,
+                    void* stream);
+
+/*
+ * tri_compact_kv - dense copy of the kept rows.
+ *
+ *   K_out[u][j] = K[row_off[u] + kept_idx[u][j]],  V_out and pos_out likewise,
+ *   for j < kept_cnt[u]; rows j >= kept_cnt[u] of the outputs are left untouched.
+ *
+ * [N] introduction: the cache is pruned to the kept entries; [R]: compressed cache entries.
+ * A byte copy (bit exact). Out of place: outputs may not overlap inputs (TRI_ERR_ALIAS).
+ *
+ *   K, V        device, [total_rows][d] elements of `dtype`
+ *   pos         device int32[total_rows], or NULL when pos_out is NULL
+ *   dtype, d    as in tri_score (d*elem_bytes must be a multiple of 16)
+ *   row_off     device int64[n_units+1]; n_units >= 1; total_rows its host copy
+ *   kept_idx    device int32[n_units][B], kept_cnt device int32[n_units] (tri_select_topb)
+ *   B           >= 0
+ *   K_out, V_out  device, [n_units][B][d] elements of `dtype`
+ *   pos_out     device int32[n_units][B], or NULL to copy no positions
+ *   stream      hipStream_t or NULL
+ * Entries of kept_idx outside 0 .. N_u-1 are skipped (their output row is left untouched).
+ */
+int tri_compact_kv(const void* K, const void* V, const int32_t* pos, int dtype, int d,
+                   const int64_t* row_off, int n_units, int64_t total_rows,
+                   const int32_t* kept_idx, const int32_t* kept_cnt, int B, void* K_out,
+                   void* V_out, int32_t* pos_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_H */

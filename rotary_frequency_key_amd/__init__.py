@@ -1,0 +1,25 @@
+"""MI355X-native key-eviction pass of TriAttention: offset-averaged trigonometric key score,
+per-unit top-B select and K/V compaction, as hand-written HIP kernels for gfx950 behind the
+C interface of ``libtri.so`` (include/tri.h).
+
+This module only marshals arguments: torch tensors -> device pointers and the current HIP
+stream. Every step of the pass runs in libtri's kernels; there is no fallback. Importing it
+fails when ``libtri.so`` has not been built.
+"""
+from ._abi import (  # noqa: F401
+    TRI_BANDS_HALF_SPLIT,
+    TRI_BANDS_INTERLEAVED,
+    TRI_DT_BF16,
+    TRI_DT_F32,
+    TRI_SELECT_HIST_FROM_SCORE,
+    PassPlan,
+    TriError,
+    library_path,
+    make_workspace,
+    prune_pass,
+    score_workspace_bytes,
+    tri_compact_kv,
+    tri_fold_weights,
+    tri_score,
+    tri_select_topb,
+)

@@ -1,0 +1,273 @@
+"""ctypes binding of libtri.so. Argument marshalling only: shapes, dtypes and devices of torch
+tensors are checked, pointers and the current stream are passed through, and a negative status
+from the library raises ``TriError``. No arithmetic of the pass happens here."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+TRI_OK = 0
+TRI_DT_F32 = 0
+TRI_DT_BF16 = 1
+TRI_BANDS_INTERLEAVED = 0
+TRI_BANDS_HALF_SPLIT = 1
+TRI_SELECT_HIST_FROM_SCORE = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libtri.so")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built: run `python -m rotary_frequency_key_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint
+    szp = ctypes.POINTER(ctypes.c_size_t)
+    lib.tri_status_string.argtypes = [i32]
+    lib.tri_status_string.restype = ctypes.c_char_p
+    lib.tri_fold_weights.argtypes = [i32, ctypes.c_double, vp, i32, vp, i32, vp, vp]
+    lib.tri_fold_weights.restype = i32
+    lib.tri_score.argtypes = [vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, vp,
+                              vp, vp, szp, vp]
+    lib.tri_score.restype = i32
+    lib.tri_select_topb.argtypes = [vp, vp, i32, i64, i64, i32, vp, vp, vp, szp, u32, vp]
+    lib.tri_select_topb.restype = i32
+    lib.tri_compact_kv.argtypes = [vp, vp, vp, i32, i32, vp, i32, i64, vp, vp, i32, vp, vp, vp, vp]
+    lib.tri_compact_kv.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+class TriError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {_lib.tri_status_string(status).decode()} (status {status})")
+
+
+def _check(fn: str, status: int):
+    if status != TRI_OK:
+        raise TriError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    return t
+
+
+def _key_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TRI_DT_BF16
+    if t.dtype == torch.float32:
+        return TRI_DT_F32
+    raise TypeError("keys/values must be bfloat16 or float32")
+
+
+# ---------------------------------------------------------------------------------------------
+
+def tri_fold_weights(d: int, theta: float, offsets, centers=None):
+    """Host fold: returns (W [F, 2] float64, mu [U, F, 2] float32 or None). ``centers`` is a
+    host array [U, F, 2] (or [U, d] with interleaved pairs) of float32, or None."""
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    F = d // 2
+    W = np.zeros((F, 2), dtype=np.float64)
+    mu = None
+    cptr, nu = None, 0
+    if centers is not None:
+        c = centers.numpy() if isinstance(centers, torch.Tensor) else np.asarray(centers)
+        c = np.ascontiguousarray(c, dtype=np.float32).reshape(-1, F, 2)
+        nu = c.shape[0]
+        mu = np.zeros((nu, F, 2), dtype=np.float32)
+        cptr = c.ctypes.data_as(ctypes.c_void_p)
+    st = _lib.tri_fold_weights(int(d), float(theta), offs.ctypes.data_as(ctypes.c_void_p),
+                               int(offs.size), cptr, int(nu), W.ctypes.data_as(ctypes.c_void_p),
+                               None if mu is None else mu.ctypes.data_as(ctypes.c_void_p))
+    _check("tri_fold_weights", st)
+    return W, mu
+
+
+def score_workspace_bytes(n_units: int) -> int:
+    """Bytes of the workspace tri_score / tri_select_topb share (histogram of the scores)."""
+    n = ctypes.c_size_t(0)
+    st = _lib.tri_score(None, TRI_DT_BF16, TRI_BANDS_INTERLEAVED, 128, 1.0, None, int(n_units), 0, 0,
+                        None, None, None, None, None, ctypes.byref(n), None)
+    _check("tri_score(query)", st)
+    return int(n.value)
+
+
+def make_workspace(n_units: int, device) -> torch.Tensor:
+    """A zero-filled workspace in its rest state (zero-filled once at allocation)."""
+    return torch.zeros(score_workspace_bytes(n_units), dtype=torch.uint8, device=device)
+
+
+def tri_score(keys: torch.Tensor, row_off: torch.Tensor, max_rows: int, pos: torch.Tensor,
+              t_now: torch.Tensor, mu: torch.Tensor, theta: float, *,
+              layout: int = TRI_BANDS_INTERLEAVED, scores: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(keys, "keys", ndim=2)
+    dt = _key_dtype(keys)
+    R, d = keys.shape
+    _dev(row_off, "row_off", torch.int64, 1)
+    U = row_off.numel() - 1
+    _dev(pos, "pos", torch.int32, 1)
+    _dev(t_now, "t_now", torch.int32, 1)
+    _dev(mu, "mu", torch.float32)
+    if pos.numel() != R or t_now.numel() != U or mu.numel() != U * d:
+        raise ValueError("pos, t_now or mu has the wrong size")
+    if scores is None:
+        scores = torch.empty(R, dtype=torch.float32, device=keys.device)
+    _dev(scores, "scores", torch.float32, 1)
+    if scores.numel() != R:
+        raise ValueError("scores has the wrong size")
+    wsp, nbytes = None, None
+    if ws is not None:
+        _dev(ws, "ws", torch.uint8, 1)
+        wsp, nbytes = _ptr(ws), ctypes.byref(ctypes.c_size_t(ws.numel()))
+    st = _lib.tri_score(_ptr(keys), dt, int(layout), int(d), float(theta), _ptr(row_off), int(U),
+                        int(R), int(max_rows), _ptr(pos), _ptr(t_now), _ptr(mu), _ptr(scores),
+                        wsp, nbytes, _stream(keys.device))
+    _check("tri_score", st)
+    return scores
+
+
+def tri_select_topb(scores: torch.Tensor, row_off: torch.Tensor, max_rows: int, B: int, *,
+                    kept_idx: Optional[torch.Tensor] = None, kept_cnt: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, hist_from_score: bool = False):
+    _dev(scores, "scores", torch.float32, 1)
+    _dev(row_off, "row_off", torch.int64, 1)
+    U = row_off.numel() - 1
+    dev = scores.device
+    if kept_idx is None:
+        kept_idx = torch.empty((U, B), dtype=torch.int32, device=dev)
+    if kept_cnt is None:
+        kept_cnt = torch.empty(U, dtype=torch.int32, device=dev)
+    _dev(kept_idx, "kept_idx", torch.int32)
+    _dev(kept_cnt, "kept_cnt", torch.int32, 1)
+    if kept_idx.numel() != U * B or kept_cnt.numel() != U:
+        raise ValueError("kept_idx or kept_cnt has the wrong size")
+    wsp, nbytes = None, None
+    if ws is not None:
+        _dev(ws, "ws", torch.uint8, 1)
+        wsp, nbytes = _ptr(ws), ctypes.byref(ctypes.c_size_t(ws.numel()))
+    flags = TRI_SELECT_HIST_FROM_SCORE if hist_from_score else 0
+    st = _lib.tri_select_topb(_ptr(scores), _ptr(row_off), int(U), int(scores.numel()), int(max_rows),
+                              int(B), _ptr(kept_idx), _ptr(kept_cnt), wsp, nbytes, flags, _stream(dev))
+    _check("tri_select_topb", st)
+    return kept_idx, kept_cnt
+
+
+def tri_compact_kv(K: torch.Tensor, V: torch.Tensor, pos: Optional[torch.Tensor], row_off: torch.Tensor,
+                   kept_idx: torch.Tensor, kept_cnt: torch.Tensor, B: int, *,
+                   K_out: Optional[torch.Tensor] = None, V_out: Optional[torch.Tensor] = None,
+                   pos_out: Optional[torch.Tensor] = None):
+    _dev(K, "K", ndim=2)
+    _dev(V, "V", ndim=2)
+    if V.dtype != K.dtype or V.shape != K.shape:
+        raise ValueError("K and V must have the same dtype and shape")
+    dt = _key_dtype(K)
+    R, d = K.shape
+    _dev(row_off, "row_off", torch.int64, 1)
+    U = row_off.numel() - 1
+    _dev(kept_idx, "kept_idx", torch.int32)
+    _dev(kept_cnt, "kept_cnt", torch.int32, 1)
+    dev = K.device
+    if K_out is None:
+        K_out = torch.zeros((U, B, d), dtype=K.dtype, device=dev)
+    if V_out is None:
+        V_out = torch.zeros((U, B, d), dtype=K.dtype, device=dev)
+    _dev(K_out, "K_out", K.dtype)
+    _dev(V_out, "V_out", K.dtype)
+    if pos is not None:
+        _dev(pos, "pos", torch.int32, 1)
+        if pos_out is None:
+            pos_out = torch.full((U, B), -1, dtype=torch.int32, device=dev)
+        _dev(pos_out, "pos_out", torch.int32)
+    if K_out.numel() != U * B * d or V_out.numel() != U * B * d:
+        raise ValueError("K_out / V_out have the wrong size")
+    st = _lib.tri_compact_kv(_ptr(K), _ptr(V), _ptr(pos), dt, int(d), _ptr(row_off), int(U), int(R),
+                             _ptr(kept_idx), _ptr(kept_cnt), int(B), _ptr(K_out), _ptr(V_out),
+                             _ptr(pos_out), _stream(dev))
+    _check("tri_compact_kv", st)
+    return K_out, V_out, pos_out
+
+
+def prune_pass(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=None, scores=None,
+               kept_idx=None, kept_cnt=None, K_out=None, V_out=None, pos_out=None,
+               layout=TRI_BANDS_INTERLEAVED):
+    """One pruning pass: score, select (using the score kernel's histogram when ``ws`` is
+    given) and compact. Returns (scores, kept_idx, kept_cnt, K_out, V_out, pos_out)."""
+    scores = tri_score(K, row_off, max_rows, pos, t_now, mu, theta, layout=layout, scores=scores, ws=ws)
+    kept_idx, kept_cnt = tri_select_topb(scores, row_off, max_rows, B, kept_idx=kept_idx,
+                                         kept_cnt=kept_cnt, ws=ws, hist_from_score=ws is not None)
+    K_out, V_out, pos_out = tri_compact_kv(K, V, pos, row_off, kept_idx, kept_cnt, B,
+                                           K_out=K_out, V_out=V_out, pos_out=pos_out)
+    return scores, kept_idx, kept_cnt, K_out, V_out, pos_out
+
+
+class PassPlan:
+    """Arguments of one pass (tri_score -> tri_select_topb -> tri_compact_kv) marshalled once,
+    for repeated launches with little host overhead. The tensors must stay alive and unchanged
+    in shape while the plan is used; launches go to the stream current at construction."""
+
+    def __init__(self, K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws, scores, kept_idx,
+                 kept_cnt, K_out, V_out, pos_out, layout=TRI_BANDS_INTERLEAVED):
+        # one checked pass through the regular entry points validates every argument
+        prune_pass(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws=ws, scores=scores,
+                   kept_idx=kept_idx, kept_cnt=kept_cnt, K_out=K_out, V_out=V_out, pos_out=pos_out,
+                   layout=layout)
+        self._keep = (K, V, pos, row_off, t_now, mu, ws, scores, kept_idx, kept_cnt, K_out, V_out, pos_out)
+        R, d = K.shape
+        U = row_off.numel() - 1
+        dt = _key_dtype(K)
+        stream = _stream(K.device)
+        self._nbytes_s = ctypes.c_size_t(ws.numel())
+        self._nbytes_t = ctypes.c_size_t(ws.numel())
+        self.score_args = (_ptr(K), dt, int(layout), int(d), float(theta), _ptr(row_off), int(U), int(R),
+                           int(max_rows), _ptr(pos), _ptr(t_now), _ptr(mu), _ptr(scores), _ptr(ws),
+                           ctypes.byref(self._nbytes_s), stream)
+        self.select_args = (_ptr(scores), _ptr(row_off), int(U), int(R), int(max_rows), int(B),
+                            _ptr(kept_idx), _ptr(kept_cnt), _ptr(ws), ctypes.byref(self._nbytes_t),
+                            TRI_SELECT_HIST_FROM_SCORE, stream)
+        self.compact_args = (_ptr(K), _ptr(V), _ptr(pos), dt, int(d), _ptr(row_off), int(U), int(R),
+                             _ptr(kept_idx), _ptr(kept_cnt), int(B), _ptr(K_out), _ptr(V_out),
+                             _ptr(pos_out), stream)
+
+    def score(self):
+        _check("tri_score", _lib.tri_score(*self.score_args))
+
+    def select(self):
+        _check("tri_select_topb", _lib.tri_select_topb(*self.select_args))
+
+    def compact(self):
+        _check("tri_compact_kv", _lib.tri_compact_kv(*self.compact_args))
+
+    def run(self):
+        self.score()
+        self.select()
+        self.compact()

@@ -161,8 +161,15 @@ def unit_inputs(wl: Workload, u: int, n_keys: int | None = None, with_values: bo
     }
 
 
-def pack_units(wl: Workload, units: Sequence[int] | None = None, lengths: Sequence[int] | None = None):
-    """Pack several units back to back.
+def _unit_job(args):
+    wl, u, n = args
+    return unit_inputs(wl, u, n)
+
+
+def pack_units(wl: Workload, units: Sequence[int] | None = None, lengths: Sequence[int] | None = None,
+               workers: int = 1):
+    """Pack several units back to back; ``workers`` > 1 generates units in a process pool
+    (spawned processes that only run this generator).
 
     Returns dict(keys [R, d], values [R, d], centers [U, d] float32, pos int32 [R],
     t int32 [U], row_off int64 [U+1], units list).
@@ -173,7 +180,15 @@ def pack_units(wl: Workload, units: Sequence[int] | None = None, lengths: Sequen
     if lengths is None:
         all_len = unit_lengths(wl)
         lengths = [int(all_len[u]) for u in units]
-    parts: List[dict] = [unit_inputs(wl, u, n) for u, n in zip(units, lengths)]
+    jobs = [(wl, u, int(n)) for u, n in zip(units, lengths)]
+    if workers > 1 and len(jobs) > 1:
+        import multiprocessing as mp
+        from concurrent.futures import ProcessPoolExecutor
+
+        with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+            parts: List[dict] = list(ex.map(_unit_job, jobs, chunksize=1))
+    else:
+        parts = [_unit_job(j) for j in jobs]
     row_off = np.zeros(len(units) + 1, dtype=np.int64)
     row_off[1:] = np.cumsum([p["keys"].shape[0] for p in parts])
     return {

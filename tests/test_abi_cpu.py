@@ -1,0 +1,151 @@
+"""Host-side tests of libtri (no GPU needed): the library loads and exports every function that
+include/tri.h declares, the host fold matches the fp64 oracle, and argument checks return their
+status codes before any HIP call (fake device addresses are never dereferenced on the host)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+tri = pytest.importorskip("rotary_frequency_key_amd")
+from rotary_frequency_key_amd import _abi  # noqa: E402
+
+lib = _abi._lib
+OK, ARG, UNSUP, ALIAS, WS = 0, -1, -2, -3, -4
+
+
+def test_exports_every_declared_function():
+    header = open(os.path.join(ROOT, "include", "tri.h")).read()
+    header = re.sub(r"/\*.*?\*/", "", header, flags=re.S)
+    declared = set(re.findall(r"\b(tri_[a-z0-9_]+)\s*\(", header))
+    assert {"tri_fold_weights", "tri_score", "tri_select_topb", "tri_compact_kv"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    for st in [0, -1, -2, -3, -4, -5, -99]:
+        assert lib.tri_status_string(st)
+
+
+def test_fold_weights_match_oracle():
+    D = O.power_of_two_offsets()
+    rng = np.random.default_rng(1)
+    for d, theta in [(128, 1e4), (128, 1e6), (128, 5e5), (64, 1e4), (256, 1e6), (8, 3.0)]:
+        centers = (rng.standard_normal((5, d)) * 2).astype(np.float32)
+        W, mu = tri.tri_fold_weights(d, theta, D, centers)
+        Wref = O.fold_weights(O.rotary_frequencies(d, theta), D)
+        # omega_f from two fp64 pow implementations may differ by an ulp; at offset 2^16 that
+        # moves the phase by <= 2^16 * 2^-52 rad, so W agrees to ~1.5e-11 / 17 per term.
+        assert np.max(np.abs(W[:, 0] + 1j * W[:, 1] - Wref)) < 1e-12
+        mref = O.folded_center(O.as_bands(centers.astype(np.float64)), Wref)
+        got = mu[..., 0].astype(np.float64) + 1j * mu[..., 1].astype(np.float64)
+        # one binary32 rounding of each component
+        err = np.abs(got - mref)
+        bound = (np.abs(mref.real) + np.abs(mref.imag)) * 2.0 ** -24 + 1e-12
+        assert np.all(err <= bound * 1.01)
+    # arbitrary schedule, including 0 and negative offsets
+    W, _ = tri.tri_fold_weights(16, 100.0, [0, -3, 5, 7, 7], None)
+    Wref = O.fold_weights(O.rotary_frequencies(16, 100.0), [0, -3, 5, 7, 7])
+    assert np.max(np.abs(W[:, 0] + 1j * W[:, 1] - Wref)) < 1e-14
+
+
+def test_fold_weights_errors():
+    W = np.zeros((64, 2))
+    D = O.power_of_two_offsets()
+    dp = D.ctypes.data_as(ctypes.c_void_p)
+    wp = W.ctypes.data_as(ctypes.c_void_p)
+    assert lib.tri_fold_weights(127, 1e4, dp, 17, None, 0, wp, None) == ARG
+    assert lib.tri_fold_weights(128, -1.0, dp, 17, None, 0, wp, None) == ARG
+    assert lib.tri_fold_weights(128, float("nan"), dp, 17, None, 0, wp, None) == ARG
+    assert lib.tri_fold_weights(128, 1e4, dp, 0, None, 0, wp, None) == ARG
+    assert lib.tri_fold_weights(128, 1e4, None, 17, None, 0, wp, None) == ARG
+    assert lib.tri_fold_weights(128, 1e4, dp, 17, None, 0, None, None) == ARG
+    assert lib.tri_fold_weights(128, 1e4, dp, 17, None, 0, wp, None) == OK
+
+
+# fake, never-dereferenced device addresses, 256-byte aligned and far apart
+A = {k: 0x10_0000_0000 * (i + 1) for i, k in enumerate(
+    ["keys", "row_off", "pos", "t", "mu", "scores", "ws", "kidx", "kcnt", "V", "Ko", "Vo", "po"])}
+
+
+def _score(**kw):
+    args = dict(keys=A["keys"], dtype=1, layout=0, d=128, theta=1e6, row_off=A["row_off"], U=8,
+                R=262144, maxr=32768, pos=A["pos"], t=A["t"], mu=A["mu"], scores=A["scores"],
+                ws=None, wsb=None)
+    args.update(kw)
+    return lib.tri_score(args["keys"], args["dtype"], args["layout"], args["d"], args["theta"],
+                         args["row_off"], args["U"], args["R"], args["maxr"], args["pos"], args["t"],
+                         args["mu"], args["scores"], args["ws"], args["wsb"], None)
+
+
+def test_score_argument_errors():
+    assert _score(dtype=7) == ARG
+    assert _score(layout=3) == ARG
+    assert _score(d=96) == UNSUP
+    assert _score(d=127) == ARG
+    assert _score(theta=0.0) == ARG
+    assert _score(U=0) == ARG
+    assert _score(R=-1) == ARG
+    assert _score(maxr=1 << 31) == ARG
+    assert _score(keys=A["keys"] + 8) == ARG  # misaligned
+    assert _score(mu=A["mu"] + 4) == ARG
+    assert _score(keys=None) == ARG
+    assert _score(row_off=None) == ARG
+    # scores overlapping the keys / positions
+    assert _score(scores=A["keys"] + 4096) == ALIAS
+    assert _score(scores=A["pos"] - 16) == ALIAS
+    # workspace protocol
+    n = ctypes.c_size_t(0)
+    assert _score(ws=None, wsb=ctypes.byref(n)) == OK and n.value == 8 * 4096 * 4
+    small = ctypes.c_size_t(n.value - 1)
+    assert _score(ws=A["ws"], wsb=ctypes.byref(small)) == WS
+    full = ctypes.c_size_t(n.value)
+    assert _score(ws=A["scores"] + 16, wsb=ctypes.byref(full)) == ALIAS
+
+
+def _select(**kw):
+    args = dict(scores=A["scores"], row_off=A["row_off"], U=8, R=262144, maxr=32768, B=2048,
+                kidx=A["kidx"], kcnt=A["kcnt"], ws=None, wsb=None, flags=0)
+    args.update(kw)
+    return lib.tri_select_topb(args["scores"], args["row_off"], args["U"], args["R"], args["maxr"],
+                               args["B"], args["kidx"], args["kcnt"], args["ws"], args["wsb"],
+                               args["flags"], None)
+
+
+def test_select_argument_errors():
+    assert _select(B=-1) == ARG
+    assert _select(U=0) == ARG
+    assert _select(flags=2) == ARG
+    assert _select(kcnt=None) == ARG
+    assert _select(kidx=None) == ARG
+    assert _select(scores=A["scores"] + 2) == ARG
+    assert _select(flags=1) == WS  # histogram requested, no workspace
+    n = ctypes.c_size_t(1)
+    assert _select(flags=1, wsb=ctypes.byref(n)) == OK and n.value == 8 * 4096 * 4
+    assert _select(flags=0, wsb=ctypes.byref(n)) == OK and n.value == 0
+    assert _select(kcnt=A["kidx"] + 64) == ALIAS
+    assert _select(kidx=A["scores"] + 64) == ALIAS
+
+
+def _compact(**kw):
+    args = dict(K=A["keys"], V=A["V"], pos=A["pos"], dtype=1, d=128, row_off=A["row_off"], U=8,
+                R=262144, kidx=A["kidx"], kcnt=A["kcnt"], B=2048, Ko=A["Ko"], Vo=A["Vo"], po=A["po"])
+    args.update(kw)
+    return lib.tri_compact_kv(args["K"], args["V"], args["pos"], args["dtype"], args["d"],
+                              args["row_off"], args["U"], args["R"], args["kidx"], args["kcnt"],
+                              args["B"], args["Ko"], args["Vo"], args["po"], None)
+
+
+def test_compact_argument_errors():
+    assert _compact(d=96) == UNSUP  # 192-byte rows
+    assert _compact(dtype=5) == ARG
+    assert _compact(B=-2) == ARG
+    assert _compact(pos=None) == ARG  # pos_out without pos
+    assert _compact(Ko=A["Ko"] + 4) == ARG
+    assert _compact(Ko=A["keys"] + 256) == ALIAS
+    assert _compact(Vo=A["Ko"] + 256) == ALIAS
+    assert _compact(po=A["kidx"]) == ALIAS
+    assert _compact(Ko=A["V"] + 1024) == ALIAS
