@@ -2,8 +2,8 @@
 """Benchmark of one key-eviction pass (score + top-B select + compaction) on one MI355X.
 
 A step is one pass over the Qwen3-8B-shaped layer workload (8 KV heads x 32768 bf16 keys,
-d = 128, theta = 1e6, offsets 2^0..2^16, B = 2048): tri_score (with the fused radix
-histogram), tri_select_topb and tri_compact_kv, all on the current stream. Inputs are resident
+d = 128, theta = 1e6, offsets 2^0..2^16, B = 2048): one tri_prune_pass call (score with the
+fused radix histogram, threshold, emit with the fused row gather), on the current stream. Inputs are resident
 in HBM; to keep the 256 MB Infinity Cache from serving them, consecutive steps rotate over
 ``--rotate`` distinct copies of the inputs and outputs (about 135 MB per copy).
 
@@ -44,7 +44,7 @@ def algorithmic_bytes(wl, n_keys_total, n_units):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ["tri_kernels.hip", "tri_internal.h"]:
+    for f in ["score.hip", "tri_device.h", "tri_internal.h"]:
         with open(os.path.join(ROOT, "rotary_frequency_key_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -157,7 +157,7 @@ def main():
             "row_off": torch.from_numpy(P["row_off"]).to(dev),
             "t": torch.from_numpy(P["t"]).to(dev),
             "mu": torch.from_numpy(mu).to(dev),
-            "ws": tri.make_workspace(U, dev),
+            "ws": tri.make_workspace(U, max_rows, dev),
             "scores": torch.empty(R, dtype=torch.float32, device=dev),
             "kept_idx": torch.empty((U, B), dtype=torch.int32, device=dev),
             "kept_cnt": torch.empty(U, dtype=torch.int32, device=dev),
@@ -172,18 +172,8 @@ def main():
         copies.append(c)
     plans = [c["plan"] for c in copies]
 
-    def step(i, ev=None):
-        plan = plans[i % len(plans)]
-        if ev is None:
-            plan.run()
-            return
-        ev[0].record()
-        plan.score()
-        ev[1].record()
-        plan.select()
-        ev[2].record()
-        plan.compact()
-        ev[3].record()
+    def step(i):
+        plans[i % len(plans)].run()
 
     for i in range(args.warmup):
         step(i)
@@ -203,14 +193,19 @@ def main():
     print(f"[bench] {args.steps} passes: {ms * 1e3:.2f} us/pass (host wall {t_wall / args.steps * 1e6:.2f} us)",
           file=sys.stderr, flush=True)
 
-    # per-kernel durations: HIP events bracket each launch on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # score kernel alone: HIP events bracket each tri_score launch on the launch stream (a
+    # separate workspace, so the pass's workspaces stay in their rest state)
+    ws_score = tri.make_workspace(U, max_rows, dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(i, evs[i])
+        c = copies[i % len(copies)]
+        evs[i][0].record()
+        tri.tri_score(c["K"], c["row_off"], max_rows, c["pos"], c["t"], c["mu"], wl.theta,
+                      scores=c["scores"], ws=None)
+        evs[i][1].record()
     torch.cuda.synchronize()
-    k_score = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    k_select = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    k_compact = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    del ws_score
+    k_score = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
 
     alg = algorithmic_bytes(wl, R, U)
     alg_total = sum(alg.values())
@@ -245,10 +240,10 @@ def main():
         "hbm_gbps": gbps,
         "hbm_frac_of_peak": gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_pass": alg_total,
-        "kernels_us": {"score": k_score, "select": k_select, "compact": k_compact},
+        "score_kernel_us": k_score,
         "roofline": {
             "bound": "hbm",
-            "kernel": "score_kernel<bf16, interleaved, 128, hist>",
+            "kernel": "score_kernel<bf16, interleaved, 128>",
             "achieved": score_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

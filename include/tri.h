@@ -24,7 +24,8 @@
  *  - All argument checks run on the host before any HIP call; when a check fails nothing is
  *    enqueued and no output is touched.
  *  - The caller owns every buffer. The library allocates no device memory and keeps no state
- *    between calls, except what a caller-provided workspace holds (tri_score/tri_select_topb).
+ *    between calls, except what a caller-provided workspace holds between the calls of one
+ *    pass (the histogram from tri_score to tri_select_topb).
  *  - Device entry points are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream). Nothing synchronises the host.
  *  - Device pointers must be 16-byte aligned unless stated otherwise.
@@ -122,7 +123,7 @@ int tri_fold_weights(int d, double theta, const int64_t* offsets, int n_offsets,
  *   ws == NULL, ws_bytes != NULL  query: *ws_bytes = required size; returns TRI_OK, no launch.
  *   both non-NULL                 *ws_bytes must be >= the required size (else
  *                                 TRI_ERR_WORKSPACE). The workspace must be in its rest state
- *                                 (all zero: zero-fill it once after allocation); the score
+ *                                 (see tri_select_topb; zero-filled once after allocation); the score
  *                                 kernel adds each unit's 12-bit top-digit histogram of the
  *                                 scores into it, and tri_select_topb called with
  *                                 TRI_SELECT_HIST_FROM_SCORE and the same ws consumes it and
@@ -153,12 +154,20 @@ int tri_score(const void* keys, int dtype, int layout, int d, double theta,
  *   kept_idx  device int32[n_units][B]: the kept rows' local indices (0 .. N_u-1) in
  *             ascending order, then -1 up to B
  *   kept_cnt  device int32[n_units]: min(B, N_u)
- *   ws, ws_bytes  workspace, same protocol as tri_score. Without
- *             TRI_SELECT_HIST_FROM_SCORE the histogram is computed here (ws may be NULL with
- *             ws_bytes NULL). With it, ws must be the workspace tri_score just filled for
- *             these scores and row_off; on return it is back in its rest state.
- *   flags     0 or TRI_SELECT_HIST_FROM_SCORE
+ *   ws        device workspace (required), 256-byte aligned, sized by the query below; it
+ *             holds the radix histogram, per-unit counters, per-chunk counts and a candidate
+ *             buffer. Its rest state has the histogram and the counters at zero (zero-filling
+ *             the whole workspace once after allocation gets there); every completed call
+ *             returns it to its rest state. Calls that share a workspace must not overlap.
+ *   ws_bytes  in/out: with ws == NULL, receives the required size (returns TRI_OK, no
+ *             launch); otherwise the size of ws (TRI_ERR_WORKSPACE if too small). The size
+ *             depends on n_units and max_rows only.
+ *   flags     0, or TRI_SELECT_HIST_FROM_SCORE when tri_score has just added the histogram
+ *             of these scores (same row_off, max_rows) into ws
  *   stream    hipStream_t or NULL
+ * Method: radix select of the B-th largest score per unit (12 + 10 + 10 bits), the last two
+ *   digits resolved among the keys of the threshold's top-digit bin; then one ordered pass
+ *   writes the kept indices. Work is split into chunks of >= 1024 rows of every unit.
  */
 int tri_select_topb(const float* scores, const int64_t* row_off, int n_units,
                     int64_t total_rows, int64_t max_rows, int B, int32_t* kept_idx,
@@ -189,6 +198,23 @@ int tri_compact_kv(const void* K, const void* V, const int32_t* pos, int dtype, 
                    const int64_t* row_off, int n_units, int64_t total_rows,
                    const int32_t* kept_idx, const int32_t* kept_cnt, int B, void* K_out,
                    void* V_out, int32_t* pos_out, void* stream);
+
+/*
+ * tri_prune_pass - one whole pruning pass: tri_score, tri_select_topb and tri_compact_kv fused
+ * into three launches (score with histogram; threshold; emit with the row gather), same
+ * results as calling the three in turn.
+ *
+ * Arguments are those of the three functions: K (the keys) and V as in tri_compact_kv, the
+ * score arguments as in tri_score, B, kept_idx and kept_cnt as in tri_select_topb, K_out /
+ * V_out / pos_out as in tri_compact_kv (pos_out may be NULL), ws / ws_bytes as in
+ * tri_select_topb (required; same query protocol). Every check of all three runs before the
+ * first launch.
+ */
+int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, double theta,
+                   const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
+                   const int32_t* pos, const int32_t* t_now, const float* mu, int B, float* scores,
+                   int32_t* kept_idx, int32_t* kept_cnt, void* K_out, void* V_out, int32_t* pos_out,
+                   void* ws, size_t* ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,8 @@ from ._abi import (  # noqa: F401
     library_path,
     make_workspace,
     prune_pass,
+    prune_pass_3calls,
+    workspace_bytes,
     score_workspace_bytes,
     tri_compact_kv,
     tri_fold_weights,

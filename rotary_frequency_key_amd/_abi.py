@@ -44,6 +44,9 @@ def _load():
     lib.tri_select_topb.restype = i32
     lib.tri_compact_kv.argtypes = [vp, vp, vp, i32, i32, vp, i32, i64, vp, vp, i32, vp, vp, vp, vp]
     lib.tri_compact_kv.restype = i32
+    lib.tri_prune_pass.argtypes = [vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, vp, i32,
+                                   vp, vp, vp, vp, vp, vp, vp, szp, vp]
+    lib.tri_prune_pass.restype = i32
     return lib
 
 
@@ -113,7 +116,7 @@ def tri_fold_weights(d: int, theta: float, offsets, centers=None):
 
 
 def score_workspace_bytes(n_units: int) -> int:
-    """Bytes of the workspace tri_score / tri_select_topb share (histogram of the scores)."""
+    """Bytes of the histogram workspace tri_score alone needs."""
     n = ctypes.c_size_t(0)
     st = _lib.tri_score(None, TRI_DT_BF16, TRI_BANDS_INTERLEAVED, 128, 1.0, None, int(n_units), 0, 0,
                         None, None, None, None, None, ctypes.byref(n), None)
@@ -121,9 +124,18 @@ def score_workspace_bytes(n_units: int) -> int:
     return int(n.value)
 
 
-def make_workspace(n_units: int, device) -> torch.Tensor:
-    """A zero-filled workspace in its rest state (zero-filled once at allocation)."""
-    return torch.zeros(score_workspace_bytes(n_units), dtype=torch.uint8, device=device)
+def workspace_bytes(n_units: int, max_rows: int) -> int:
+    """Bytes of the workspace of tri_select_topb / tri_prune_pass (it also serves tri_score)."""
+    n = ctypes.c_size_t(0)
+    st = _lib.tri_select_topb(None, None, int(n_units), 0, int(max_rows), 0, None, None, None,
+                              ctypes.byref(n), 0, None)
+    _check("tri_select_topb(query)", st)
+    return int(n.value)
+
+
+def make_workspace(n_units: int, max_rows: int, device) -> torch.Tensor:
+    """A workspace in its rest state (zero-filled once, at allocation)."""
+    return torch.zeros(workspace_bytes(n_units, max_rows), dtype=torch.uint8, device=device)
 
 
 def tri_score(keys: torch.Tensor, row_off: torch.Tensor, max_rows: int, pos: torch.Tensor,
@@ -171,10 +183,12 @@ def tri_select_topb(scores: torch.Tensor, row_off: torch.Tensor, max_rows: int, 
     _dev(kept_cnt, "kept_cnt", torch.int32, 1)
     if kept_idx.numel() != U * B or kept_cnt.numel() != U:
         raise ValueError("kept_idx or kept_cnt has the wrong size")
-    wsp, nbytes = None, None
-    if ws is not None:
-        _dev(ws, "ws", torch.uint8, 1)
-        wsp, nbytes = _ptr(ws), ctypes.byref(ctypes.c_size_t(ws.numel()))
+    if ws is None:
+        if hist_from_score:
+            raise ValueError("hist_from_score needs the workspace tri_score filled")
+        ws = make_workspace(U, max_rows, dev)
+    _dev(ws, "ws", torch.uint8, 1)
+    wsp, nbytes = _ptr(ws), ctypes.byref(ctypes.c_size_t(ws.numel()))
     flags = TRI_SELECT_HIST_FROM_SCORE if hist_from_score else 0
     st = _lib.tri_select_topb(_ptr(scores), _ptr(row_off), int(U), int(scores.numel()), int(max_rows),
                               int(B), _ptr(kept_idx), _ptr(kept_cnt), wsp, nbytes, flags, _stream(dev))
@@ -217,57 +231,92 @@ def tri_compact_kv(K: torch.Tensor, V: torch.Tensor, pos: Optional[torch.Tensor]
     return K_out, V_out, pos_out
 
 
+def _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, kept_idx, kept_cnt,
+               K_out, V_out, pos_out, layout):
+    _dev(K, "K", ndim=2)
+    _dev(V, "V", ndim=2)
+    if V.dtype != K.dtype or V.shape != K.shape:
+        raise ValueError("K and V must have the same dtype and shape")
+    dt = _key_dtype(K)
+    R, d = K.shape
+    dev = K.device
+    _dev(row_off, "row_off", torch.int64, 1)
+    U = row_off.numel() - 1
+    _dev(pos, "pos", torch.int32, 1)
+    _dev(t_now, "t_now", torch.int32, 1)
+    _dev(mu, "mu", torch.float32)
+    if pos.numel() != R or t_now.numel() != U or mu.numel() != U * d:
+        raise ValueError("pos, t_now or mu has the wrong size")
+    if ws is None:
+        ws = make_workspace(U, max_rows, dev)
+    if scores is None:
+        scores = torch.empty(R, dtype=torch.float32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((U, B), dtype=torch.int32, device=dev)
+    if kept_cnt is None:
+        kept_cnt = torch.empty(U, dtype=torch.int32, device=dev)
+    if K_out is None:
+        K_out = torch.zeros((U, B, d), dtype=K.dtype, device=dev)
+    if V_out is None:
+        V_out = torch.zeros((U, B, d), dtype=K.dtype, device=dev)
+    if pos_out is None:
+        pos_out = torch.full((U, B), -1, dtype=torch.int32, device=dev)
+    _dev(ws, "ws", torch.uint8, 1)
+    _dev(scores, "scores", torch.float32, 1)
+    _dev(kept_idx, "kept_idx", torch.int32)
+    _dev(kept_cnt, "kept_cnt", torch.int32, 1)
+    _dev(K_out, "K_out", K.dtype)
+    _dev(V_out, "V_out", K.dtype)
+    _dev(pos_out, "pos_out", torch.int32)
+    if (scores.numel() != R or kept_idx.numel() != U * B or kept_cnt.numel() != U
+            or K_out.numel() != U * B * d or V_out.numel() != U * B * d or pos_out.numel() != U * B):
+        raise ValueError("an output has the wrong size")
+    tensors = (K, V, pos, row_off, t_now, mu, ws, scores, kept_idx, kept_cnt, K_out, V_out, pos_out)
+    nbytes = ctypes.c_size_t(ws.numel())
+    args = (_ptr(K), _ptr(V), dt, int(layout), int(d), float(theta), _ptr(row_off), int(U), int(R),
+            int(max_rows), _ptr(pos), _ptr(t_now), _ptr(mu), int(B), _ptr(scores), _ptr(kept_idx),
+            _ptr(kept_cnt), _ptr(K_out), _ptr(V_out), _ptr(pos_out), _ptr(ws), ctypes.byref(nbytes),
+            _stream(dev))
+    return tensors, nbytes, args
+
+
 def prune_pass(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=None, scores=None,
                kept_idx=None, kept_cnt=None, K_out=None, V_out=None, pos_out=None,
                layout=TRI_BANDS_INTERLEAVED):
-    """One pruning pass: score, select (using the score kernel's histogram when ``ws`` is
-    given) and compact. Returns (scores, kept_idx, kept_cnt, K_out, V_out, pos_out)."""
+    """One pruning pass through tri_prune_pass (score, select and compaction, three launches).
+    Returns (scores, kept_idx, kept_cnt, K_out, V_out, pos_out)."""
+    tensors, nbytes, args = _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores,
+                                       kept_idx, kept_cnt, K_out, V_out, pos_out, layout)
+    _check("tri_prune_pass", _lib.tri_prune_pass(*args))
+    return tensors[7], tensors[8], tensors[9], tensors[10], tensors[11], tensors[12]
+
+
+def prune_pass_3calls(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=None, scores=None,
+                      kept_idx=None, kept_cnt=None, K_out=None, V_out=None, pos_out=None,
+                      layout=TRI_BANDS_INTERLEAVED):
+    """The same pass as three separate calls: tri_score (histogram into ws), tri_select_topb
+    (using that histogram) and tri_compact_kv."""
+    U = row_off.numel() - 1
+    if ws is None:
+        ws = make_workspace(U, max_rows, K.device)
     scores = tri_score(K, row_off, max_rows, pos, t_now, mu, theta, layout=layout, scores=scores, ws=ws)
     kept_idx, kept_cnt = tri_select_topb(scores, row_off, max_rows, B, kept_idx=kept_idx,
-                                         kept_cnt=kept_cnt, ws=ws, hist_from_score=ws is not None)
+                                         kept_cnt=kept_cnt, ws=ws, hist_from_score=True)
     K_out, V_out, pos_out = tri_compact_kv(K, V, pos, row_off, kept_idx, kept_cnt, B,
                                            K_out=K_out, V_out=V_out, pos_out=pos_out)
     return scores, kept_idx, kept_cnt, K_out, V_out, pos_out
 
 
 class PassPlan:
-    """Arguments of one pass (tri_score -> tri_select_topb -> tri_compact_kv) marshalled once,
-    for repeated launches with little host overhead. The tensors must stay alive and unchanged
-    in shape while the plan is used; launches go to the stream current at construction."""
+    """Arguments of tri_prune_pass marshalled once, for repeated launches with little host
+    overhead. The tensors are held by the plan; launches go to the stream current at
+    construction."""
 
     def __init__(self, K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws, scores, kept_idx,
                  kept_cnt, K_out, V_out, pos_out, layout=TRI_BANDS_INTERLEAVED):
-        # one checked pass through the regular entry points validates every argument
-        prune_pass(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws=ws, scores=scores,
-                   kept_idx=kept_idx, kept_cnt=kept_cnt, K_out=K_out, V_out=V_out, pos_out=pos_out,
-                   layout=layout)
-        self._keep = (K, V, pos, row_off, t_now, mu, ws, scores, kept_idx, kept_cnt, K_out, V_out, pos_out)
-        R, d = K.shape
-        U = row_off.numel() - 1
-        dt = _key_dtype(K)
-        stream = _stream(K.device)
-        self._nbytes_s = ctypes.c_size_t(ws.numel())
-        self._nbytes_t = ctypes.c_size_t(ws.numel())
-        self.score_args = (_ptr(K), dt, int(layout), int(d), float(theta), _ptr(row_off), int(U), int(R),
-                           int(max_rows), _ptr(pos), _ptr(t_now), _ptr(mu), _ptr(scores), _ptr(ws),
-                           ctypes.byref(self._nbytes_s), stream)
-        self.select_args = (_ptr(scores), _ptr(row_off), int(U), int(R), int(max_rows), int(B),
-                            _ptr(kept_idx), _ptr(kept_cnt), _ptr(ws), ctypes.byref(self._nbytes_t),
-                            TRI_SELECT_HIST_FROM_SCORE, stream)
-        self.compact_args = (_ptr(K), _ptr(V), _ptr(pos), dt, int(d), _ptr(row_off), int(U), int(R),
-                             _ptr(kept_idx), _ptr(kept_cnt), int(B), _ptr(K_out), _ptr(V_out),
-                             _ptr(pos_out), stream)
-
-    def score(self):
-        _check("tri_score", _lib.tri_score(*self.score_args))
-
-    def select(self):
-        _check("tri_select_topb", _lib.tri_select_topb(*self.select_args))
-
-    def compact(self):
-        _check("tri_compact_kv", _lib.tri_compact_kv(*self.compact_args))
+        self._tensors, self._nbytes, self._args = _pass_args(
+            K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, kept_idx, kept_cnt,
+            K_out, V_out, pos_out, layout)
 
     def run(self):
-        self.score()
-        self.select()
-        self.compact()
+        _check("tri_prune_pass", _lib.tri_prune_pass(*self._args))

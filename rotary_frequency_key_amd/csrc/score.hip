@@ -1,37 +1,28 @@
-// Device kernels of libtri for gfx950 (CDNA4, wave64) and their launchers.
+// Score kernel of libtri for gfx950 (CDNA4, wave64).
 //
-//  score_kernel    streams the keys once, 16 lanes per 128-d row, one 16-byte load per lane
-//                  per row; per band: fixed-point rotation phase, hardware sine/cosine in
-//                  revolutions, two-term bf16 dot products with mu'; DPP row reduction.
-//                  Optionally folds a 12-bit top-digit histogram of the scores per unit.
-//  select_kernel   one workgroup per unit: radix select of the B-th largest order key
-//                  (12 + 10 + 10 bits), then one ordered pass that emits kept row indices
-//                  ascending with the lower-index tie rule.
-//  compact_kernel  gathers the kept K/V rows (16-byte loads/stores) and positions.
+// Streams every key once: 16 lanes per 128-d row (4 rotary bands per lane), one 16-byte load
+// per lane per row. Per band: the rotation phase in 23-bit fixed point plus a binary32
+// residual, hardware sine and cosine in revolutions, two-term bf16 dot products with the
+// offset-averaged center; the 16 partial sums of a row are added with DPP. Optionally adds a
+// 12-bit top-digit histogram of the scores per unit (the first radix digit of the select).
 //
-// Score definition: "The future-offset average in TriAttention can be precomputed", sections
-// "The same score, read as arrows in the plane" and "The averaging step": per key,
+// Score: "The future-offset average in TriAttention can be precomputed", sections "The same
+// score, read as arrows in the plane" and "The averaging step": per key,
 //     Re{ sum_f mu'_f conj(k_f) e^{i omega_f delta} }
 //   = sum_f x_f cos(omega_f delta) - y_f sin(omega_f delta),
 //     x_f = Re(mu'_f) Re(k_f) + Im(mu'_f) Im(k_f),  y_f = Im(mu'_f) Re(k_f) - Re(mu'_f) Im(k_f).
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "tri_internal.h"
+#include "tri_device.h"
 
 namespace tri {
 namespace {
 
-constexpr int kDtF32 = 0;
-constexpr int kDtBf16 = 1;
-constexpr int kInterleaved = 0;
-constexpr int kHalfSplit = 1;
+using dev::kDtBf16;
+using dev::kDtF32;
+using dev::kHalfSplit;
+using dev::kInterleaved;
+using dev::order_key;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// ---------------------------------------------------------------------------------------------
-// small helpers
-// ---------------------------------------------------------------------------------------------
 
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
   const uint32_t b = __float_as_uint(x);
@@ -64,16 +55,6 @@ __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
   return r;
 }
 
-// Total order on binary32 scores as unsigned integers: larger score -> larger key;
-// -0.0 and +0.0 map to one key; every NaN maps to 0, below -inf (0x007FFFFF).
-__device__ __forceinline__ uint32_t order_key(float s) {
-  const uint32_t b = __float_as_uint(s);
-  const uint32_t mag = b & 0x7FFFFFFFu;
-  if (mag > 0x7F800000u) return 0u;
-  if (mag == 0u) return 0x80000000u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -92,10 +73,6 @@ __device__ __forceinline__ float group_sum(float v) {
   }
   return v;
 }
-
-// ---------------------------------------------------------------------------------------------
-// score
-// ---------------------------------------------------------------------------------------------
 
 // Loads this lane's 4 bands of one row and returns, per band, the pair (Re k, Im k).
 // bf16: one dword per band holding (re, im) as a bf16 pair (re in the low half).
@@ -217,10 +194,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int c
 
   const int unit = blockIdx.x / chunks_per_unit;
   const int chunk = blockIdx.x - unit * chunks_per_unit;
-  int64_t beg = a.row_off[unit], end = a.row_off[unit + 1];
-  beg = beg < 0 ? 0 : (beg > a.total_rows ? a.total_rows : beg);
-  end = end < beg ? beg : (end > a.total_rows ? a.total_rows : end);
-  if (end - beg > a.max_rows) end = beg + a.max_rows;
+  const dev::UnitRows ur = dev::unit_rows(a.row_off, unit, a.total_rows, a.max_rows);
+  const int64_t beg = ur.beg, end = ur.beg + ur.n;
   const int64_t r0 = beg + (int64_t)chunk * RPB;
   if (r0 >= end) return;  // uniform across the block
   const int64_t r1 = (end - r0 < RPB) ? end : r0 + RPB;
@@ -354,185 +329,6 @@ hipError_t launch_score_d(const ScoreArgs& a, const BandConst& bc, hipStream_t s
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// select
-// ---------------------------------------------------------------------------------------------
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-// Exclusive prefix sum over the block; *total receives the block sum. sh: >= NT/64 words.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const uint32_t inc = wave_incl_scan(v);
-  if (lane == 63) sh[wid] = inc;
-  __syncthreads();
-  if (wid == 0) {
-    uint32_t w = lane < NW ? sh[lane] : 0u;
-    w = wave_incl_scan(w);
-    if (lane < NW) sh[lane] = w;
-  }
-  __syncthreads();
-  const uint32_t base = wid ? sh[wid - 1] : 0u;
-  *total = sh[NW - 1];
-  __syncthreads();
-  return base + inc - v;
-}
-
-// In h[0..nb): find bin b with above(b) < rank <= above(b) + h[b], above(b) = sum of bins > b.
-// Requires sum(h) >= rank >= 1. Returns b; *above_out = above(b).
-template <int NT>
-__device__ uint32_t find_bin(const uint32_t* h, int nb, uint32_t rank, uint32_t* sh, uint32_t* found,
-                             uint32_t* above_out) {
-  const int per = nb / NT;  // nb is a multiple of NT
-  const int top = nb - 1 - (int)threadIdx.x * per;
-  uint32_t loc = 0;
-  for (int q = 0; q < per; ++q) loc += h[top - q];
-  uint32_t tot;
-  uint32_t c = block_excl_scan<NT>(loc, sh, &tot);
-  for (int q = 0; q < per; ++q) {
-    const uint32_t hb = h[top - q];
-    if (c < rank && rank <= c + hb) { found[0] = (uint32_t)(top - q); found[1] = c; }
-    c += hb;
-  }
-  __syncthreads();
-  const uint32_t b = found[0];
-  *above_out = found[1];
-  __syncthreads();
-  return b;
-}
-
-constexpr int kSelectThreads = 1024;
-
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
-  constexpr int NT = kSelectThreads;
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t sh[NT / 64];
-  __shared__ uint32_t found[2];
-
-  const int u = blockIdx.x;
-  if (threadIdx.x == 0) { found[0] = 0u; found[1] = 0u; }
-  int64_t beg = a.row_off[u], end = a.row_off[u + 1];
-  beg = beg < 0 ? 0 : (beg > a.total_rows ? a.total_rows : beg);
-  end = end < beg ? beg : (end > a.total_rows ? a.total_rows : end);
-  if (end - beg > a.max_rows) end = beg + a.max_rows;
-  const int n = (int)(end - beg);
-  const int m = a.B < n ? a.B : n;
-  int32_t* out = a.kept_idx + (int64_t)u * a.B;
-  uint32_t* gh = a.hist ? a.hist + (size_t)u * kHistBins : nullptr;
-  const float* s = a.scores + beg;
-
-  if (m == n || m == 0) {  // keep every row, or none
-    for (int j = threadIdx.x; j < a.B; j += NT) out[j] = j < m ? j : -1;
-    if (threadIdx.x == 0) a.kept_cnt[u] = m;
-    if (a.hist_ready)
-      for (int i = threadIdx.x; i < kHistBins; i += NT) gh[i] = 0u;
-    return;
-  }
-
-  // digit 1: bits 31..20
-  if (a.hist_ready) {
-    for (int i = threadIdx.x; i < kHistBins; i += NT) { h[i] = gh[i]; gh[i] = 0u; }
-  } else {
-    for (int i = threadIdx.x; i < kHistBins; i += NT) h[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&h[order_key(s[i]) >> 20], 1u);
-  }
-  __syncthreads();
-  uint32_t rank = (uint32_t)m, above;
-  const uint32_t b0 = find_bin<NT>(h, kHistBins, rank, sh, found, &above);
-  rank -= above;
-
-  // digit 2: bits 19..10 of keys whose digit 1 is b0
-  for (int i = threadIdx.x; i < 1024; i += NT) h[i] = 0u;
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint32_t k = order_key(s[i]);
-    if ((k >> 20) == b0) atomicAdd(&h[(k >> 10) & 1023u], 1u);
-  }
-  __syncthreads();
-  const uint32_t b1 = find_bin<NT>(h, 1024, rank, sh, found, &above);
-  rank -= above;
-  const uint32_t pre = (b0 << 10) | b1;  // bits 31..10
-
-  // digit 3: bits 9..0 of keys whose bits 31..10 are pre
-  for (int i = threadIdx.x; i < 1024; i += NT) h[i] = 0u;
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint32_t k = order_key(s[i]);
-    if ((k >> 10) == pre) atomicAdd(&h[k & 1023u], 1u);
-  }
-  __syncthreads();
-  const uint32_t b2 = find_bin<NT>(h, 1024, rank, sh, found, &above);
-  rank -= above;
-  const uint32_t T = (pre << 10) | b2;  // order key of the B-th largest score
-  const uint32_t need = rank;           // keys equal to T that are kept (the lowest indices)
-
-  // ordered emission: slot of a kept key = (# greater keys before it) + (# kept ties before it)
-  uint32_t run_gt = 0, run_eq = 0;
-  for (int base = 0; base < n; base += NT) {
-    const int i = base + threadIdx.x;
-    const uint32_t k = i < n ? order_key(s[i]) : 0u;
-    const uint32_t gt = (i < n && k > T) ? 1u : 0u;
-    const uint32_t eq = (i < n && k == T) ? 1u : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<NT>((gt << 16) | eq, sh, &tot);
-    const uint32_t G = run_gt + (ex >> 16), E = run_eq + (ex & 0xFFFFu);
-    // slots stay below m by construction; the bound also holds for a stale histogram
-    const uint32_t slot = G + (E < need ? E : need);
-    if ((gt || (eq && E < need)) && slot < (uint32_t)m) out[slot] = i;
-    run_gt += tot >> 16;
-    run_eq += tot & 0xFFFFu;
-  }
-  for (int j = m + threadIdx.x; j < a.B; j += NT) out[j] = -1;
-  if (threadIdx.x == 0) a.kept_cnt[u] = m;
-}
-
-// ---------------------------------------------------------------------------------------------
-// compact
-// ---------------------------------------------------------------------------------------------
-
-constexpr int kCompactThreads = 256;
-constexpr int kCompactRows = 64;  // kept rows per block
-
-template <int CPR>  // 16-byte chunks per row
-__global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a, int blocks_per_unit) {
-  const int u = blockIdx.x / blocks_per_unit;
-  const int b = blockIdx.x - u * blocks_per_unit;
-  int64_t beg = a.row_off[u], end = a.row_off[u + 1];
-  beg = beg < 0 ? 0 : (beg > a.total_rows ? a.total_rows : beg);
-  end = end < beg ? beg : (end > a.total_rows ? a.total_rows : end);
-  const int64_t n = end - beg;
-  int cnt = a.kept_cnt[u];
-  cnt = cnt < 0 ? 0 : (cnt > a.B ? a.B : cnt);
-  const int j0 = b * kCompactRows;
-  const uint4* K = static_cast<const uint4*>(a.K);
-  const uint4* V = static_cast<const uint4*>(a.V);
-  uint4* Ko = static_cast<uint4*>(a.K_out);
-  uint4* Vo = static_cast<uint4*>(a.V_out);
-  for (int q = threadIdx.x; q < kCompactRows * CPR; q += kCompactThreads) {
-    const int j = j0 + q / CPR;
-    const int c = q % CPR;
-    if (j >= cnt) break;
-    const int32_t src = a.kept_idx[(int64_t)u * a.B + j];
-    if (src < 0 || src >= n) continue;
-    const int64_t srow = beg + src;
-    const int64_t drow = (int64_t)u * a.B + j;
-    Ko[drow * CPR + c] = K[srow * CPR + c];
-    Vo[drow * CPR + c] = V[srow * CPR + c];
-    if (c == 0 && a.pos_out) a.pos_out[drow] = a.pos[srow];
-  }
-}
-
 }  // namespace
 
 hipError_t launch_score(const ScoreArgs& a, const BandConst& bc, hipStream_t s) {
@@ -542,26 +338,6 @@ hipError_t launch_score(const ScoreArgs& a, const BandConst& bc, hipStream_t s) 
   }
   return a.layout == kInterleaved ? launch_score_d<kDtF32, kInterleaved>(a, bc, s)
                                   : launch_score_d<kDtF32, kHalfSplit>(a, bc, s);
-}
-
-hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.n_units), dim3(kSelectThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
-  if (a.B == 0) return hipSuccess;
-  const int64_t bpu = (a.B + kCompactRows - 1) / kCompactRows;
-  const int64_t grid = bpu * a.n_units;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  switch (a.row_bytes / 16) {
-    case 8: hipLaunchKernelGGL(compact_kernel<8>, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a, (int)bpu); break;
-    case 16: hipLaunchKernelGGL(compact_kernel<16>, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a, (int)bpu); break;
-    case 32: hipLaunchKernelGGL(compact_kernel<32>, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a, (int)bpu); break;
-    case 64: hipLaunchKernelGGL(compact_kernel<64>, dim3((unsigned)grid), dim3(kCompactThreads), 0, s, a, (int)bpu); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 }  // namespace tri

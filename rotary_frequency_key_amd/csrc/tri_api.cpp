@@ -1,5 +1,6 @@
 // C entry points of libtri: host-side argument checks, the offline fold (fp64), the per-band
-// rotation constants, and the kernel launches. Every check runs before the first HIP call.
+// rotation constants, and the kernel launches. Every check of a call runs before its first HIP
+// call; a failed check enqueues nothing.
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -24,7 +25,7 @@ Range span(const void* p, int64_t bytes) {
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
-size_t hist_bytes(int n_units) { return static_cast<size_t>(n_units) * tri::kHistBins * sizeof(uint32_t); }
+bool finite_positive(double x) { return std::isfinite(x) && x > 0.0; }
 
 // omega_f = theta^(-2f/d): "The future-offset average in TriAttention can be precomputed",
 // section "The score TriAttention computes".
@@ -45,7 +46,96 @@ void band_constants(int d, double theta, tri::BandConst* bc) {
   }
 }
 
-bool finite_positive(double x) { return std::isfinite(x) && x > 0.0; }
+// ---- argument checks (no HIP calls) ------------------------------------------------------------
+
+int check_score(const void* keys, int dtype, int layout, int d, double theta, const int64_t* row_off,
+                int n_units, int64_t total_rows, int64_t max_rows, const int32_t* pos, const int32_t* t_now,
+                const float* mu, const float* scores, const void* hist, size_t hist_bytes) {
+  if (n_units < 1 || total_rows < 0 || max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
+  if (dtype != TRI_DT_F32 && dtype != TRI_DT_BF16) return TRI_ERR_ARG;
+  if (layout != TRI_BANDS_INTERLEAVED && layout != TRI_BANDS_HALF_SPLIT) return TRI_ERR_ARG;
+  if (!finite_positive(theta)) return TRI_ERR_ARG;
+  if (d < 2 || (d % 2) != 0) return TRI_ERR_ARG;
+  if (d != 64 && d != 128 && d != 256) return TRI_ERR_UNSUPPORTED;
+  if (row_off == nullptr || !aligned(row_off, 8)) return TRI_ERR_ARG;
+  if (t_now == nullptr || mu == nullptr || !aligned(t_now, 4) || !aligned(mu, 16)) return TRI_ERR_ARG;
+  if (total_rows > 0) {
+    if (keys == nullptr || pos == nullptr || scores == nullptr) return TRI_ERR_ARG;
+    if (!aligned(keys, 16) || !aligned(pos, 4) || !aligned(scores, 4)) return TRI_ERR_ARG;
+  }
+  if (hist != nullptr && !aligned(hist, 256)) return TRI_ERR_ARG;
+  const int elem = dtype == TRI_DT_BF16 ? 2 : 4;
+  const Range ins[] = {span(keys, total_rows * d * elem), span(pos, total_rows * 4),
+                       span(mu, int64_t(n_units) * d * 4), span(t_now, int64_t(n_units) * 4),
+                       span(row_off, int64_t(n_units + 1) * 8)};
+  const Range out = span(scores, total_rows * 4);
+  const Range h = span(hist, hist ? static_cast<int64_t>(hist_bytes) : 0);
+  for (const Range& r : ins)
+    if (overlap(out, r) || overlap(h, r)) return TRI_ERR_ALIAS;
+  if (overlap(out, h)) return TRI_ERR_ALIAS;
+  return TRI_OK;
+}
+
+int check_select(const float* scores, const int64_t* row_off, int n_units, int64_t total_rows,
+                 int64_t max_rows, int B, const int32_t* kept_idx, const int32_t* kept_cnt, const void* ws,
+                 size_t ws_total) {
+  if (n_units < 1 || total_rows < 0 || max_rows < 0 || max_rows >= (int64_t(1) << 31) || B < 0)
+    return TRI_ERR_ARG;
+  if (row_off == nullptr || !aligned(row_off, 8)) return TRI_ERR_ARG;
+  if (kept_cnt == nullptr || !aligned(kept_cnt, 4)) return TRI_ERR_ARG;
+  if (B > 0 && (kept_idx == nullptr || !aligned(kept_idx, 4))) return TRI_ERR_ARG;
+  if (total_rows > 0 && (scores == nullptr || !aligned(scores, 4))) return TRI_ERR_ARG;
+  if (!aligned(ws, 256)) return TRI_ERR_ARG;
+  const Range ki = span(kept_idx, int64_t(n_units) * B * 4);
+  const Range kc = span(kept_cnt, int64_t(n_units) * 4);
+  const Range in_s = span(scores, total_rows * 4);
+  const Range in_r = span(row_off, int64_t(n_units + 1) * 8);
+  const Range w = span(ws, static_cast<int64_t>(ws_total));
+  if (overlap(ki, kc) || overlap(ki, in_s) || overlap(ki, in_r) || overlap(kc, in_s) || overlap(kc, in_r) ||
+      overlap(w, ki) || overlap(w, kc) || overlap(w, in_s) || overlap(w, in_r))
+    return TRI_ERR_ALIAS;
+  return TRI_OK;
+}
+
+// Compaction outputs: K_out/V_out [n_units][B] rows, pos_out [n_units][B] or null. `others` are
+// further ranges the outputs may not overlap.
+int check_compact(const void* K, const void* V, const int32_t* pos, int dtype, int d, int n_units,
+                  int64_t total_rows, int B, const void* K_out, const void* V_out, const int32_t* pos_out,
+                  const Range* others, int n_others, int* row_bytes_out) {
+  if (dtype != TRI_DT_F32 && dtype != TRI_DT_BF16) return TRI_ERR_ARG;
+  if (d < 2 || (d % 2) != 0) return TRI_ERR_ARG;
+  const int row_bytes = d * (dtype == TRI_DT_BF16 ? 2 : 4);
+  if (row_bytes != 128 && row_bytes != 256 && row_bytes != 512 && row_bytes != 1024) return TRI_ERR_UNSUPPORTED;
+  if (B > 0) {
+    if (K_out == nullptr || V_out == nullptr || !aligned(K_out, 16) || !aligned(V_out, 16)) return TRI_ERR_ARG;
+    if (pos_out != nullptr && ((total_rows > 0 && pos == nullptr) || !aligned(pos_out, 4))) return TRI_ERR_ARG;
+  }
+  if (total_rows > 0) {
+    if (K == nullptr || V == nullptr || !aligned(K, 16) || !aligned(V, 16)) return TRI_ERR_ARG;
+    if (pos != nullptr && !aligned(pos, 4)) return TRI_ERR_ARG;
+  }
+  const int64_t out_rows = int64_t(n_units) * B;
+  const Range ko = span(K_out, out_rows * row_bytes), vo = span(V_out, out_rows * row_bytes);
+  const Range po = span(pos_out, out_rows * 4);
+  const Range ins[] = {span(K, total_rows * row_bytes), span(V, total_rows * row_bytes), span(pos, total_rows * 4)};
+  for (const Range& r : ins)
+    if (overlap(ko, r) || overlap(vo, r) || overlap(po, r)) return TRI_ERR_ALIAS;
+  for (int i = 0; i < n_others; ++i)
+    if (overlap(ko, others[i]) || overlap(vo, others[i]) || overlap(po, others[i])) return TRI_ERR_ALIAS;
+  if (overlap(ko, vo) || overlap(ko, po) || overlap(vo, po)) return TRI_ERR_ALIAS;
+  *row_bytes_out = row_bytes;
+  return TRI_OK;
+}
+
+hipError_t launch_score_call(const void* keys, int dtype, int layout, int d, double theta, const int64_t* row_off,
+                             int n_units, int64_t total_rows, int64_t max_rows, const int32_t* pos,
+                             const int32_t* t_now, const float* mu, float* scores, void* hist, hipStream_t s) {
+  tri::BandConst bc;
+  band_constants(d, theta, &bc);
+  tri::ScoreArgs a{keys, dtype, layout, d, row_off, n_units, total_rows, max_rows,
+                   pos, t_now, mu, scores, static_cast<uint32_t*>(hist)};
+  return tri::launch_score(a, bc, s);
+}
 
 }  // namespace
 
@@ -102,48 +192,22 @@ int tri_score(const void* keys, int dtype, int layout, int d, double theta,
               const int32_t* pos, const int32_t* t_now, const float* mu, float* scores,
               void* ws, size_t* ws_bytes, void* stream) {
   if (n_units < 1) return TRI_ERR_ARG;
-  const size_t need = hist_bytes(n_units);
+  const size_t need = tri::hist_bytes(n_units);
   if (ws == nullptr && ws_bytes != nullptr) {  // size query
     *ws_bytes = need;
     return TRI_OK;
   }
-  if (total_rows < 0 || max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
-  if (dtype != TRI_DT_F32 && dtype != TRI_DT_BF16) return TRI_ERR_ARG;
-  if (layout != TRI_BANDS_INTERLEAVED && layout != TRI_BANDS_HALF_SPLIT) return TRI_ERR_ARG;
-  if (!finite_positive(theta)) return TRI_ERR_ARG;
-  if (d < 2 || (d % 2) != 0) return TRI_ERR_ARG;
-  if (d != 64 && d != 128 && d != 256) return TRI_ERR_UNSUPPORTED;
-  if (row_off == nullptr || !aligned(row_off, 8)) return TRI_ERR_ARG;
-  if (t_now == nullptr || mu == nullptr || !aligned(t_now, 4) || !aligned(mu, 16)) return TRI_ERR_ARG;
-  if (total_rows > 0) {
-    if (keys == nullptr || pos == nullptr || scores == nullptr) return TRI_ERR_ARG;
-    if (!aligned(keys, 16) || !aligned(pos, 4) || !aligned(scores, 4)) return TRI_ERR_ARG;
-  }
-  uint32_t* hist = nullptr;
+  void* hist = nullptr;
   if (ws_bytes != nullptr) {
     if (*ws_bytes < need) return TRI_ERR_WORKSPACE;
-    if (!aligned(ws, 16)) return TRI_ERR_ARG;
-    hist = static_cast<uint32_t*>(ws);
+    hist = ws;
   }
-  const int elem = dtype == TRI_DT_BF16 ? 2 : 4;
-  const Range out = span(scores, total_rows * 4);
-  if (overlap(out, span(keys, total_rows * d * elem)) || overlap(out, span(pos, total_rows * 4)) ||
-      overlap(out, span(mu, int64_t(n_units) * d * 4)) || overlap(out, span(t_now, int64_t(n_units) * 4)) ||
-      overlap(out, span(row_off, int64_t(n_units + 1) * 8)))
-    return TRI_ERR_ALIAS;
-  if (hist) {
-    const Range h = span(hist, static_cast<int64_t>(need));
-    if (overlap(h, out) || overlap(h, span(keys, total_rows * d * elem)) || overlap(h, span(pos, total_rows * 4)) ||
-        overlap(h, span(mu, int64_t(n_units) * d * 4)) || overlap(h, span(t_now, int64_t(n_units) * 4)) ||
-        overlap(h, span(row_off, int64_t(n_units + 1) * 8)))
-      return TRI_ERR_ALIAS;
-  }
-
-  tri::BandConst bc;
-  band_constants(d, theta, &bc);
-  tri::ScoreArgs a{keys, dtype, layout, d, row_off, n_units, total_rows, max_rows,
-                   pos, t_now, mu, scores, hist};
-  if (tri::launch_score(a, bc, static_cast<hipStream_t>(stream)) != hipSuccess) return TRI_ERR_HIP;
+  const int st = check_score(keys, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now,
+                             mu, scores, hist, need);
+  if (st != TRI_OK) return st;
+  if (launch_score_call(keys, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu,
+                        scores, hist, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return TRI_ERR_HIP;
   return TRI_OK;
 }
 
@@ -152,34 +216,22 @@ int tri_select_topb(const float* scores, const int64_t* row_off, int n_units,
                     int32_t* kept_cnt, void* ws, size_t* ws_bytes, unsigned flags,
                     void* stream) {
   if (n_units < 1 || (flags & ~TRI_SELECT_HIST_FROM_SCORE) != 0) return TRI_ERR_ARG;
-  const bool from_score = (flags & TRI_SELECT_HIST_FROM_SCORE) != 0;
-  const size_t need = from_score ? hist_bytes(n_units) : 0;
+  if (max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
+  const tri::WsLayout lay = tri::ws_layout(n_units, max_rows);
+  const size_t total = lay.total;
   if (ws == nullptr && ws_bytes != nullptr) {  // size query
-    *ws_bytes = need;
+    *ws_bytes = total;
     return TRI_OK;
   }
-  if (total_rows < 0 || max_rows < 0 || max_rows >= (int64_t(1) << 31) || B < 0) return TRI_ERR_ARG;
-  if (row_off == nullptr || !aligned(row_off, 8)) return TRI_ERR_ARG;
-  if (kept_cnt == nullptr || !aligned(kept_cnt, 4)) return TRI_ERR_ARG;
-  if (B > 0 && (kept_idx == nullptr || !aligned(kept_idx, 4))) return TRI_ERR_ARG;
-  if (total_rows > 0 && (scores == nullptr || !aligned(scores, 4))) return TRI_ERR_ARG;
-  uint32_t* hist = nullptr;
-  if (from_score) {
-    if (ws == nullptr || ws_bytes == nullptr || *ws_bytes < need) return TRI_ERR_WORKSPACE;
-    if (!aligned(ws, 16)) return TRI_ERR_ARG;
-    hist = static_cast<uint32_t*>(ws);
-  }
-  const Range ki = span(kept_idx, int64_t(n_units) * B * 4);
-  const Range kc = span(kept_cnt, int64_t(n_units) * 4);
-  const Range in_s = span(scores, total_rows * 4);
-  const Range in_r = span(row_off, int64_t(n_units + 1) * 8);
-  if (overlap(ki, kc) || overlap(ki, in_s) || overlap(ki, in_r) || overlap(kc, in_s) || overlap(kc, in_r))
-    return TRI_ERR_ALIAS;
-  if (hist) {
-    const Range h = span(hist, static_cast<int64_t>(need));
-    if (overlap(h, ki) || overlap(h, kc) || overlap(h, in_s) || overlap(h, in_r)) return TRI_ERR_ALIAS;
-  }
-  tri::SelectArgs a{scores, row_off, n_units, total_rows, max_rows, B, kept_idx, kept_cnt, hist, from_score};
+  const int st = check_select(scores, row_off, n_units, total_rows, max_rows, B, kept_idx, kept_cnt, ws, total);
+  if (st != TRI_OK) return st;
+  if (ws == nullptr || ws_bytes == nullptr || *ws_bytes < total) return TRI_ERR_WORKSPACE;
+  tri::SelectArgs a{};
+  a.scores = scores; a.row_off = row_off; a.n_units = n_units; a.total_rows = total_rows;
+  a.max_rows = max_rows; a.B = B; a.kept_idx = kept_idx; a.kept_cnt = kept_cnt;
+  a.ws = ws;
+  a.lay = lay;
+  a.hist_ready = (flags & TRI_SELECT_HIST_FROM_SCORE) != 0;
   if (tri::launch_select(a, static_cast<hipStream_t>(stream)) != hipSuccess) return TRI_ERR_HIP;
   return TRI_OK;
 }
@@ -189,35 +241,68 @@ int tri_compact_kv(const void* K, const void* V, const int32_t* pos, int dtype, 
                    const int32_t* kept_idx, const int32_t* kept_cnt, int B, void* K_out,
                    void* V_out, int32_t* pos_out, void* stream) {
   if (n_units < 1 || total_rows < 0 || B < 0) return TRI_ERR_ARG;
-  if (dtype != TRI_DT_F32 && dtype != TRI_DT_BF16) return TRI_ERR_ARG;
-  if (d < 2 || (d % 2) != 0) return TRI_ERR_ARG;
-  const int elem = dtype == TRI_DT_BF16 ? 2 : 4;
-  const int row_bytes = d * elem;
-  if (row_bytes != 128 && row_bytes != 256 && row_bytes != 512 && row_bytes != 1024) return TRI_ERR_UNSUPPORTED;
   if (row_off == nullptr || !aligned(row_off, 8)) return TRI_ERR_ARG;
   if (kept_cnt == nullptr || !aligned(kept_cnt, 4)) return TRI_ERR_ARG;
-  if (B > 0 && pos_out != nullptr && pos == nullptr) return TRI_ERR_ARG;
-  if (B > 0) {
-    if (kept_idx == nullptr || K_out == nullptr || V_out == nullptr) return TRI_ERR_ARG;
-    if (!aligned(kept_idx, 4) || !aligned(K_out, 16) || !aligned(V_out, 16)) return TRI_ERR_ARG;
-    if (pos_out != nullptr && !aligned(pos_out, 4)) return TRI_ERR_ARG;
-  }
-  if (total_rows > 0) {
-    if (K == nullptr || V == nullptr || !aligned(K, 16) || !aligned(V, 16)) return TRI_ERR_ARG;
-    if (pos != nullptr && !aligned(pos, 4)) return TRI_ERR_ARG;
-  }
+  if (B > 0 && (kept_idx == nullptr || !aligned(kept_idx, 4))) return TRI_ERR_ARG;
   const int64_t out_rows = int64_t(n_units) * B;
-  const Range ko = span(K_out, out_rows * row_bytes), vo = span(V_out, out_rows * row_bytes);
-  const Range po = span(pos_out, out_rows * 4);
-  const Range ins[] = {span(K, total_rows * row_bytes), span(V, total_rows * row_bytes),
-                       span(pos, total_rows * 4), span(row_off, int64_t(n_units + 1) * 8),
-                       span(kept_idx, out_rows * 4), span(kept_cnt, int64_t(n_units) * 4)};
-  for (const Range& r : ins)
-    if (overlap(ko, r) || overlap(vo, r) || overlap(po, r)) return TRI_ERR_ALIAS;
-  if (overlap(ko, vo) || overlap(ko, po) || overlap(vo, po)) return TRI_ERR_ALIAS;
+  const Range others[] = {span(row_off, int64_t(n_units + 1) * 8), span(kept_idx, out_rows * 4),
+                          span(kept_cnt, int64_t(n_units) * 4)};
+  int row_bytes = 0;
+  const int st = check_compact(K, V, pos, dtype, d, n_units, total_rows, B, K_out, V_out, pos_out, others, 3,
+                               &row_bytes);
+  if (st != TRI_OK) return st;
   tri::CompactArgs a{K, V, pos, row_bytes, row_off, n_units, total_rows, kept_idx, kept_cnt, B,
                      K_out, V_out, pos_out};
   if (tri::launch_compact(a, static_cast<hipStream_t>(stream)) != hipSuccess) return TRI_ERR_HIP;
+  return TRI_OK;
+}
+
+int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, double theta,
+                   const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
+                   const int32_t* pos, const int32_t* t_now, const float* mu, int B, float* scores,
+                   int32_t* kept_idx, int32_t* kept_cnt, void* K_out, void* V_out, int32_t* pos_out,
+                   void* ws, size_t* ws_bytes, void* stream) {
+  if (n_units < 1 || max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
+  const tri::WsLayout lay = tri::ws_layout(n_units, max_rows);
+  const size_t total = lay.total;
+  if (ws == nullptr && ws_bytes != nullptr) {  // size query
+    *ws_bytes = total;
+    return TRI_OK;
+  }
+  int st = check_score(K, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu, scores,
+                       ws, total);
+  if (st != TRI_OK) return st;
+  st = check_select(scores, row_off, n_units, total_rows, max_rows, B, kept_idx, kept_cnt, ws, total);
+  if (st != TRI_OK) return st;
+  const int64_t out_rows = int64_t(n_units) * B;
+  const Range others[] = {span(row_off, int64_t(n_units + 1) * 8), span(t_now, int64_t(n_units) * 4),
+                          span(mu, int64_t(n_units) * d * 4), span(scores, total_rows * 4),
+                          span(kept_idx, out_rows * 4), span(kept_cnt, int64_t(n_units) * 4),
+                          span(ws, static_cast<int64_t>(total))};
+  int row_bytes = 0;
+  st = check_compact(K, V, pos, dtype, d, n_units, total_rows, B, K_out, V_out, pos_out, others, 7, &row_bytes);
+  if (st != TRI_OK) return st;
+  // scores vs kept_idx / kept_cnt: the one pair of outputs the checks above do not compare
+  if (overlap(span(scores, total_rows * 4), span(kept_idx, out_rows * 4)) ||
+      overlap(span(scores, total_rows * 4), span(kept_cnt, int64_t(n_units) * 4)))
+    return TRI_ERR_ALIAS;
+  if (ws == nullptr || ws_bytes == nullptr || *ws_bytes < total) return TRI_ERR_WORKSPACE;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_score_call(K, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu, scores,
+                        ws, s) != hipSuccess)
+    return TRI_ERR_HIP;
+  tri::SelectArgs a{};
+  a.scores = scores; a.row_off = row_off; a.n_units = n_units; a.total_rows = total_rows;
+  a.max_rows = max_rows; a.B = B; a.kept_idx = kept_idx; a.kept_cnt = kept_cnt;
+  a.ws = ws;
+  a.lay = lay;
+  a.hist_ready = true;
+  if (B > 0) {
+    a.K = K; a.V = V; a.pos = pos; a.row_bytes = row_bytes;
+    a.K_out = K_out; a.V_out = V_out; a.pos_out = pos_out;
+  }
+  if (tri::launch_select(a, s) != hipSuccess) return TRI_ERR_HIP;
   return TRI_OK;
 }
 

@@ -32,8 +32,8 @@ def keys_to_host(t, dtype):
     return t.cpu().numpy()
 
 
-def run_gpu(P, wl, B, *, use_ws=True, layout=0, centers=None, theta=None, offsets=None,
-            keys=None, max_rows=None, prefill=True):
+def run_gpu(P, wl, B, *, layout=0, centers=None, theta=None, offsets=None,
+            keys=None, max_rows=None, path="fused"):
     """One pass through the library. Returns a dict of host numpy arrays."""
     import rotary_frequency_key_amd as tri
 
@@ -52,14 +52,24 @@ def run_gpu(P, wl, B, *, use_ws=True, layout=0, centers=None, theta=None, offset
     lens = np.diff(P["row_off"])
     if max_rows is None:
         max_rows = int(lens.max()) if lens.size else 0
-    ws = tri.make_workspace(U, dev) if use_ws else None
+    ws = tri.make_workspace(U, max_rows, dev)
     # sentinel-filled outputs: rows past kept_cnt must stay untouched
     K_out = torch.full((U, B, wl.d), 123.5, dtype=K.dtype, device=dev)
     V_out = torch.full_like(K_out, -77.0)
     pos_out = torch.full((U, B), -5, dtype=torch.int32, device=dev)
-    scores, kept_idx, kept_cnt, K_out, V_out, pos_out = tri.prune_pass(
-        K, V, pos, row_off, max_rows, t_now, mu_d, theta, B, ws=ws, K_out=K_out, V_out=V_out,
-        pos_out=pos_out, layout=layout)
+    if path == "fused":  # tri_prune_pass
+        scores, kept_idx, kept_cnt, K_out, V_out, pos_out = tri.prune_pass(
+            K, V, pos, row_off, max_rows, t_now, mu_d, theta, B, ws=ws, K_out=K_out, V_out=V_out,
+            pos_out=pos_out, layout=layout)
+    elif path == "calls":  # tri_score (histogram) -> tri_select_topb -> tri_compact_kv
+        scores, kept_idx, kept_cnt, K_out, V_out, pos_out = tri.prune_pass_3calls(
+            K, V, pos, row_off, max_rows, t_now, mu_d, theta, B, ws=ws, K_out=K_out, V_out=V_out,
+            pos_out=pos_out, layout=layout)
+    else:  # tri_score without histogram -> standalone tri_select_topb -> tri_compact_kv
+        scores = tri.tri_score(K, row_off, max_rows, pos, t_now, mu_d, theta, layout=layout)
+        kept_idx, kept_cnt = tri.tri_select_topb(scores, row_off, max_rows, B, ws=ws)
+        K_out, V_out, pos_out = tri.tri_compact_kv(K, V, pos, row_off, kept_idx, kept_cnt, B,
+                                                   K_out=K_out, V_out=V_out, pos_out=pos_out)
     torch.cuda.synchronize()
     out = {
         "scores": scores.cpu().numpy(),
@@ -70,9 +80,14 @@ def run_gpu(P, wl, B, *, use_ws=True, layout=0, centers=None, theta=None, offset
         "pos_out": pos_out.cpu().numpy(),
         "mu": mu,
     }
-    if ws is not None:
-        out["ws_after"] = ws.cpu().numpy()
+    out["ws_after"] = ws_at_rest(ws.cpu().numpy(), U)
     return out
+
+
+def ws_at_rest(ws, U):
+    """True when the workspace is in its rest state: the per-unit top-digit histograms (its
+    first U * 4096 words) are zero. The rest of the workspace is scratch."""
+    return bool(np.all(ws.view(np.uint32)[:U * 4096] == 0))
 
 
 def widen(keys, dtype):

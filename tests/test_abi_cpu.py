@@ -103,7 +103,8 @@ def test_score_argument_errors():
     small = ctypes.c_size_t(n.value - 1)
     assert _score(ws=A["ws"], wsb=ctypes.byref(small)) == WS
     full = ctypes.c_size_t(n.value)
-    assert _score(ws=A["scores"] + 16, wsb=ctypes.byref(full)) == ALIAS
+    assert _score(ws=A["scores"] + 256, wsb=ctypes.byref(full)) == ALIAS
+    assert _score(ws=A["ws"] + 16, wsb=ctypes.byref(full)) == ARG  # 256-byte alignment
 
 
 def _select(**kw):
@@ -122,12 +123,47 @@ def test_select_argument_errors():
     assert _select(kcnt=None) == ARG
     assert _select(kidx=None) == ARG
     assert _select(scores=A["scores"] + 2) == ARG
-    assert _select(flags=1) == WS  # histogram requested, no workspace
+    assert _select(flags=1) == WS  # no workspace
+    assert _select(flags=0) == WS
     n = ctypes.c_size_t(1)
-    assert _select(flags=1, wsb=ctypes.byref(n)) == OK and n.value == 8 * 4096 * 4
-    assert _select(flags=0, wsb=ctypes.byref(n)) == OK and n.value == 0
-    assert _select(kcnt=A["kidx"] + 64) == ALIAS
-    assert _select(kidx=A["scores"] + 64) == ALIAS
+    assert _select(flags=1, wsb=ctypes.byref(n)) == OK
+    size = n.value
+    # histograms, unit states, per-chunk offsets and tie counts (32 chunks of 1024 rows)
+    assert size == 8 * 4096 * 4 + 256 + 2 * 1024
+    n2 = ctypes.c_size_t(0)
+    assert _select(flags=0, wsb=ctypes.byref(n2)) == OK and n2.value == size
+    ok = ctypes.c_size_t(size)
+    assert _select(ws=A["ws"], wsb=ctypes.byref(ctypes.c_size_t(size - 1))) == WS
+    assert _select(ws=A["ws"] + 128, wsb=ctypes.byref(ok)) == ARG  # 256-byte alignment
+    assert _select(ws=A["scores"] + 256, wsb=ctypes.byref(ok)) == ALIAS
+    assert _select(kcnt=A["kidx"] + 64, ws=A["ws"], wsb=ctypes.byref(ok)) == ALIAS
+    assert _select(kidx=A["scores"] + 64, ws=A["ws"], wsb=ctypes.byref(ok)) == ALIAS
+
+
+def _prune(**kw):
+    n = ctypes.c_size_t(1 << 40)
+    args = dict(K=A["keys"], V=A["V"], dtype=1, layout=0, d=128, theta=1e6, row_off=A["row_off"], U=8,
+                R=262144, maxr=32768, pos=A["pos"], t=A["t"], mu=A["mu"], B=2048, scores=A["scores"],
+                kidx=A["kidx"], kcnt=A["kcnt"], Ko=A["Ko"], Vo=A["Vo"], po=A["po"], ws=A["ws"],
+                wsb=ctypes.byref(n))
+    args.update(kw)
+    return lib.tri_prune_pass(*args.values(), None)
+
+
+def test_prune_pass_argument_errors():
+    n = ctypes.c_size_t(0)
+    assert _prune(ws=None, wsb=ctypes.byref(n)) == OK and n.value > 0
+    assert _prune(ws=None, wsb=None) == WS
+    assert _prune(wsb=ctypes.byref(ctypes.c_size_t(16))) == WS
+    assert _prune(dtype=3) == ARG
+    assert _prune(d=96) == UNSUP
+    assert _prune(B=-1) == ARG
+    assert _prune(Ko=A["keys"]) == ALIAS
+    assert _prune(Vo=A["scores"]) == ALIAS
+    assert _prune(po=A["ws"] + 64) == ALIAS
+    assert _prune(scores=A["kidx"]) == ALIAS
+    assert _prune(kcnt=A["scores"] + 64) == ALIAS
+    assert _prune(V=A["V"] + 8) == ARG
 
 
 def _compact(**kw):

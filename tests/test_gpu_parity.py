@@ -28,7 +28,7 @@ def test_c1_full():
     out = run_gpu(P, wl, wl.budget)
     err, mism = check_unit(P, 0, wl, out, wl.budget, label="c1")
     say(f"c1 score err {err:.3g}, kept mismatches in band {mism}")
-    assert np.all(out["ws_after"] == 0)  # workspace back at rest
+    assert out["ws_after"]  # workspace back at rest
 
 
 def test_c2_full():
@@ -41,11 +41,13 @@ def test_c2_full():
         err, mism = check_unit(P, i, wl, out, wl.budget, label="c2")
         worst, total = max(worst, err), total + mism
     say(f"c2 worst score err {worst:.3g}, kept mismatches in band {total}")
-    assert np.all(out["ws_after"] == 0)
-    # the standalone select (own histogram) keeps the same rows
-    out2 = run_gpu(P, wl, wl.budget, use_ws=False)
-    assert np.array_equal(out2["scores"], out["scores"])
-    assert np.array_equal(out2["kept_idx"], out["kept_idx"])
+    assert out["ws_after"]
+    # the three separate calls, and the standalone select (its own histogram), give the same bits
+    for path in ["calls", "standalone"]:
+        out2 = run_gpu(P, wl, wl.budget, path=path)
+        for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
+            assert np.array_equal(out2[k], out[k]), (path, k)
+        assert out2["ws_after"], path
     # deterministic: a second pass is bitwise identical
     out3 = run_gpu(P, wl, wl.budget)
     for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
@@ -91,7 +93,19 @@ def test_edge_cases_ragged_units():
         out = run_gpu(P, wl, B)
         for i in range(len(lengths)):
             check_unit(P, i, wl, out, B, label=f"edge B={B}")
-        assert np.all(out["ws_after"] == 0)
+        assert out["ws_after"]
+
+
+def test_all_units_empty():
+    """No rows at all (zero-size inputs): every unit keeps nothing, outputs stay untouched."""
+    wl = dataclasses.replace(workload("c2"), heads=3)
+    P = pack_units(wl, [0, 1, 2], [0, 0, 0])
+    say("case all units empty")
+    for path in ["fused", "calls", "standalone"]:
+        out = run_gpu(P, wl, 16, path=path)
+        assert np.all(out["kept_cnt"] == 0) and np.all(out["kept_idx"] == -1), path
+        assert np.all(out["pos_out"] == -5), path
+        assert out["ws_after"], path
 
 
 def test_zero_center_all_ties():
@@ -106,6 +120,39 @@ def test_zero_center_all_ties():
     assert np.array_equal(out["kept_idx"][0], np.arange(1000))
     s_ref, scale = oracle_unit(P, 1, wl, centers=centers)
     check_unit(P, 1, wl, out, 1000, s_ref=s_ref, scale=scale, label="zero-center")
+
+
+def test_zero_center_large_tie_group():
+    """40000 tied keys: more candidates than the candidate buffer holds (the fallback path)."""
+    wl = workload("c2")
+    P = pack_units(wl, [0, 1, 2], [40000, 9000, 70000])
+    centers = P["centers"].copy()
+    centers[0] = 0.0
+    centers[2] = 0.0
+    say("case zero center, 40000 and 70000 ties")
+    for path in ["fused", "calls"]:
+        out = run_gpu(P, wl, 2048, centers=centers, path=path)
+        assert np.array_equal(out["kept_idx"][0], np.arange(2048))
+        assert np.array_equal(out["kept_idx"][2], np.arange(2048))
+        s_ref, scale = oracle_unit(P, 1, wl, centers=centers)
+        check_unit(P, 1, wl, out, 2048, s_ref=s_ref, scale=scale, label=f"zero-center-large {path}")
+        assert out["ws_after"]
+
+
+def test_quantized_scores_heavy_ties():
+    """Keys drawn from few values so that many scores tie exactly; kept rows must follow the
+    lower-index rule across chunk boundaries."""
+    wl = dataclasses.replace(workload("c2"), heads=2)
+    P = pack_units(wl, [0, 1], [50000, 7000])
+    rng = np.random.default_rng(33)
+    from synthgen import f32_to_bf16_bits
+    P["keys"] = f32_to_bf16_bits(rng.choice([-1.0, 0.5, 2.0], size=P["keys"].shape).astype(np.float32))
+    P["pos"] = np.zeros_like(P["pos"])  # one distance: scores depend on the key only
+    say("case quantized keys")
+    for path in ["fused", "calls"]:
+        out = run_gpu(P, wl, 3000, path=path)
+        for i in range(2):
+            check_unit(P, i, wl, out, 3000, label=f"quantized {path}")
 
 
 def test_half_split_layout_matches_interleaved():
