@@ -149,16 +149,18 @@ int tri_score(const void* keys, int dtype, int layout, int d, double theta,
  *   row_off   device int64[n_units+1] (as in tri_score)
  *   n_units   >= 1
  *   total_rows host copy of row_off[n_units]
- *   max_rows  host bound on every N_u; must be < 2^31
+ *   max_rows  host bound on every N_u; must be < 2^31 (TRI_ERR_ARG); above 2^27 the select
+ *             is not implemented (TRI_ERR_UNSUPPORTED)
  *   B         budget per unit, 0 <= B < 2^31
  *   kept_idx  device int32[n_units][B]: the kept rows' local indices (0 .. N_u-1) in
  *             ascending order, then -1 up to B
  *   kept_cnt  device int32[n_units]: min(B, N_u)
- *   ws        device workspace (required), 256-byte aligned, sized by the query below; it
- *             holds the radix histogram, per-unit counters, per-chunk counts and a candidate
- *             buffer. Its rest state has the histogram and the counters at zero (zero-filling
- *             the whole workspace once after allocation gets there); every completed call
- *             returns it to its rest state. Calls that share a workspace must not overlap.
+ *   ws        device workspace (required), 256-byte aligned, sized by the query below (about
+ *             4 bytes per row of max_rows per unit, plus 16 KB per unit); it holds the radix
+ *             histograms, per-granule counts and the candidates. Its rest state has the
+ *             histograms at zero (zero-filling the whole workspace once after allocation gets
+ *             there); every completed call returns it to its rest state. Calls that share a
+ *             workspace must not overlap.
  *   ws_bytes  in/out: with ws == NULL, receives the required size (returns TRI_OK, no
  *             launch); otherwise the size of ws (TRI_ERR_WORKSPACE if too small). The size
  *             depends on n_units and max_rows only.
@@ -167,7 +169,8 @@ int tri_score(const void* keys, int dtype, int layout, int d, double theta,
  *   stream    hipStream_t or NULL
  * Method: radix select of the B-th largest score per unit (12 + 10 + 10 bits), the last two
  *   digits resolved among the keys of the threshold's top-digit bin; then one ordered pass
- *   writes the kept indices. Work is split into chunks of >= 1024 rows of every unit.
+ *   writes the kept indices. Every unit is split into workgroups of >= 1024 rows for the
+ *   threshold and into granules of >= 64 rows for the output pass.
  */
 int tri_select_topb(const float* scores, const int64_t* row_off, int n_units,
                     int64_t total_rows, int64_t max_rows, int B, int32_t* kept_idx,
@@ -201,8 +204,8 @@ int tri_compact_kv(const void* K, const void* V, const int32_t* pos, int dtype, 
 
 /*
  * tri_prune_pass - one whole pruning pass: tri_score, tri_select_topb and tri_compact_kv fused
- * into three launches (score with histogram; threshold; emit with the row gather), same
- * results as calling the three in turn.
+ * into four launches (score with histogram; candidates; threshold; emit with the row gather),
+ * same results as calling the three in turn.
  *
  * Arguments are those of the three functions: K (the keys) and V as in tri_compact_kv, the
  * score arguments as in tri_score, B, kept_idx and kept_cnt as in tri_select_topb, K_out /

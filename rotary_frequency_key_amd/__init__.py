@@ -13,6 +13,7 @@ from ._abi import (  # noqa: F401
     TRI_DT_F32,
     TRI_SELECT_HIST_FROM_SCORE,
     PassPlan,
+    ScorePlan,
     TriError,
     library_path,
     make_workspace,

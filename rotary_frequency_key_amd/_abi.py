@@ -283,7 +283,7 @@ def _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, ke
 def prune_pass(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=None, scores=None,
                kept_idx=None, kept_cnt=None, K_out=None, V_out=None, pos_out=None,
                layout=TRI_BANDS_INTERLEAVED):
-    """One pruning pass through tri_prune_pass (score, select and compaction, three launches).
+    """One pruning pass through tri_prune_pass (score, select and compaction, four launches).
     Returns (scores, kept_idx, kept_cnt, K_out, V_out, pos_out)."""
     tensors, nbytes, args = _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores,
                                        kept_idx, kept_cnt, K_out, V_out, pos_out, layout)
@@ -305,6 +305,37 @@ def prune_pass_3calls(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=N
     K_out, V_out, pos_out = tri_compact_kv(K, V, pos, row_off, kept_idx, kept_cnt, B,
                                            K_out=K_out, V_out=V_out, pos_out=pos_out)
     return scores, kept_idx, kept_cnt, K_out, V_out, pos_out
+
+
+class ScorePlan:
+    """Arguments of tri_score marshalled once, for repeated launches with little host overhead
+    (used to time the score kernel alone). With ws, every launch adds its histogram into ws."""
+
+    def __init__(self, keys, row_off, max_rows, pos, t_now, mu, theta, *, scores, ws=None,
+                 layout=TRI_BANDS_INTERLEAVED):
+        _dev(keys, "keys", ndim=2)
+        dt = _key_dtype(keys)
+        R, d = keys.shape
+        _dev(row_off, "row_off", torch.int64, 1)
+        U = row_off.numel() - 1
+        _dev(pos, "pos", torch.int32, 1)
+        _dev(t_now, "t_now", torch.int32, 1)
+        _dev(mu, "mu", torch.float32)
+        _dev(scores, "scores", torch.float32, 1)
+        if pos.numel() != R or t_now.numel() != U or mu.numel() != U * d or scores.numel() != R:
+            raise ValueError("pos, t_now, mu or scores has the wrong size")
+        wsp, self._nbytes = None, None
+        if ws is not None:
+            _dev(ws, "ws", torch.uint8, 1)
+            self._nbytes = ctypes.c_size_t(ws.numel())
+            wsp = _ptr(ws)
+        self._tensors = (keys, row_off, pos, t_now, mu, scores, ws)
+        self._args = (_ptr(keys), dt, int(layout), int(d), float(theta), _ptr(row_off), int(U), int(R),
+                      int(max_rows), _ptr(pos), _ptr(t_now), _ptr(mu), _ptr(scores), wsp,
+                      None if ws is None else ctypes.byref(self._nbytes), _stream(keys.device))
+
+    def run(self):
+        _check("tri_score", _lib.tri_score(*self._args))
 
 
 class PassPlan:

@@ -81,6 +81,7 @@ int check_select(const float* scores, const int64_t* row_off, int n_units, int64
                  size_t ws_total) {
   if (n_units < 1 || total_rows < 0 || max_rows < 0 || max_rows >= (int64_t(1) << 31) || B < 0)
     return TRI_ERR_ARG;
+  if (max_rows > tri::kMaxSelectRows) return TRI_ERR_UNSUPPORTED;
   if (row_off == nullptr || !aligned(row_off, 8)) return TRI_ERR_ARG;
   if (kept_cnt == nullptr || !aligned(kept_cnt, 4)) return TRI_ERR_ARG;
   if (B > 0 && (kept_idx == nullptr || !aligned(kept_idx, 4))) return TRI_ERR_ARG;

@@ -116,6 +116,29 @@ __device__ __forceinline__ uint32_t block_excl_scan_dpp(uint32_t v, uint32_t* sh
   return (wid ? sh[NW + wid - 1] : 0u) + inc - v;
 }
 
+// Two exclusive prefix sums over a block of NT threads sharing two barriers. sh: >= 4 * NT/64
+// words of LDS. *ta, *tb receive the block sums. Call from every thread.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2_dpp(uint32_t a, uint32_t b, uint32_t* sh, uint32_t* ea,
+                                                     uint32_t* eb, uint32_t* ta, uint32_t* tb) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t ia = wave_incl_scan_dpp(a), ib = wave_incl_scan_dpp(b);
+  if (lane == 63) { sh[wid] = ia; sh[NW + wid] = ib; }
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t x = lane < NW ? sh[lane] : 0u, y = lane < NW ? sh[NW + lane] : 0u;
+    x = wave_incl_scan_dpp(x);
+    y = wave_incl_scan_dpp(y);
+    if (lane < NW) { sh[2 * NW + lane] = x; sh[3 * NW + lane] = y; }
+  }
+  __syncthreads();
+  *ta = sh[3 * NW - 1];
+  *tb = sh[4 * NW - 1];
+  *ea = (wid ? sh[2 * NW + wid - 1] : 0u) + ia - a;
+  *eb = (wid ? sh[3 * NW + wid - 1] : 0u) + ib - b;
+}
+
 template <int NT>
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* sh) {
   uint32_t tot;

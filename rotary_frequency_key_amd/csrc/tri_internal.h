@@ -12,14 +12,17 @@ constexpr int kMaxBands = 128;     // d <= 256 on the device path
 constexpr int kHistBins = 4096;    // top radix digit: bits 31..20 of the order key
 constexpr int kHistShift = 20;
 
-// Select: candidates (keys in the threshold's top-digit bin) buffered in LDS up to kCandCap,
-// beyond which the last two digits are counted from the scores directly. Units are cut into
-// chunks of chunk_rows rows (a power of two >= 1024) so that no unit has more than kMaxChunks.
-constexpr int kCandCap = 8192;
-constexpr int kChunkMin = 1024;
-constexpr int kMaxChunks = 2048;
-// Output slots per workgroup of the emit / gather kernel.
-constexpr int kSlots = 64;
+// Select. Rows of a unit are cut into granules of 2^gran_shift rows (64, doubled until a unit of
+// max_rows rows has at most kMaxGran of them); the emit kernel gives each granule one wave. The
+// candidate kernel gives each workgroup 2^cand_shift rows (max(1024, granule)) and collects the
+// keys whose top digit is the threshold's ("candidates"); the resolve kernel stages up to
+// kCandCap of them in LDS (beyond that it reads the scores again). Per-granule counts are kept
+// in 16 bits, so granules are at most 2^15 rows and units at most kMaxSelectRows rows.
+constexpr int kGranMinShift = 6;
+constexpr int kMaxGran = 4096;
+constexpr int kCandRowsShift = 10;
+constexpr int kCandCap = 4096;
+constexpr int64_t kMaxSelectRows = int64_t(kMaxGran) << 15;
 
 // Per-band rotation constants of tri_score. The phase of band f at distance delta is
 // frac(delta * omega_f / 2pi) revolutions, evaluated as
@@ -32,41 +35,53 @@ struct BandConst {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Per-unit result of the threshold kernel, read by the emit kernel.
+// Per-unit select state. b0/above0: written by the candidate kernel (the threshold's top digit
+// and the count of keys in higher bins); T/need/mode/m: written by the resolve kernel.
 struct UnitState {
-  uint32_t T;     // order key of the B-th largest score
-  uint32_t need;  // rows equal to T that are kept (the lowest indices)
-  uint32_t mode;  // kModeThreshold / kModeAll / kModeNone
-  uint32_t m;     // rows kept: min(B, N_u)
+  uint32_t T;       // order key of the B-th largest score
+  uint32_t need;    // rows equal to T that are kept (the lowest indices)
+  uint32_t mode;    // kModeThreshold / kModeAll / kModeNone
+  uint32_t m;       // rows kept: min(B, N_u)
+  uint32_t b0;      // top digit of T
+  uint32_t above0;  // keys whose top digit is above b0
+  uint32_t pad[2];
 };
 constexpr uint32_t kModeThreshold = 0, kModeAll = 1, kModeNone = 2;
 
 // Workspace: per-unit top-digit histograms [n_units][kHistBins] (zero at rest: the score kernel
-// adds into them, the threshold kernel reads and clears them), then scratch written before it
-// is read in every call: unit states, per-chunk output offsets and per-chunk counts of ties
-// before the chunk. The histograms come first so that tri_score's workspace is a prefix.
+// or the histogram kernel adds into them, the candidate kernel reads them, the resolve kernel
+// clears them), then scratch that every call writes before it reads it: unit states,
+// per-candidate-workgroup candidate counts, the candidates (one word per row: low 20 bits of the
+// key above the granule index), and per granule the keys above the top digit, the output offset
+// and the ties before it. The histograms come first so that tri_score's workspace is a prefix.
 struct WsLayout {
-  int chunk_rows, chunk_shift, chunks;
-  size_t hist, state, chunk_off, chunk_eq, total;
+  int gran_shift, grans;     // granule rows = 2^gran_shift; granules per unit (>= 1)
+  int cand_shift, cand_wgs;  // candidate workgroup rows = 2^cand_shift; workgroups per unit (>= 1)
+  size_t hist, state, wg_cnt, cand, gran_gt, gran_off, gran_eq, total;
 };
 
 inline size_t hist_bytes(int n_units) { return (size_t)n_units * kHistBins * 4; }
 
 inline WsLayout ws_layout(int n_units, int64_t max_rows) {
   WsLayout L{};
-  int64_t cr = kChunkMin;
-  while (cr * kMaxChunks < max_rows) cr *= 2;
-  L.chunk_rows = (int)cr;
-  L.chunk_shift = 0;
-  while ((int64_t(1) << L.chunk_shift) < cr) ++L.chunk_shift;
-  const int64_t ch = (max_rows + cr - 1) / cr;
-  L.chunks = ch < 1 ? 1 : (int)ch;
+  int gs = kGranMinShift;
+  while ((int64_t(kMaxGran) << gs) < max_rows) ++gs;
+  L.gran_shift = gs;
+  const int64_t ng = (max_rows + (int64_t(1) << gs) - 1) >> gs;
+  L.grans = ng < 1 ? 1 : (int)ng;
+  const int cs = gs > kCandRowsShift ? gs : kCandRowsShift;
+  L.cand_shift = cs;
+  const int64_t nw = (max_rows + (int64_t(1) << cs) - 1) >> cs;
+  L.cand_wgs = nw < 1 ? 1 : (int)nw;
   const size_t U = (size_t)n_units;
   size_t off = 0;
-  L.hist = off;      off = align256(off + hist_bytes(n_units));
-  L.state = off;     off = align256(off + U * sizeof(UnitState));
-  L.chunk_off = off; off = align256(off + U * L.chunks * 4);
-  L.chunk_eq = off;  off = align256(off + U * L.chunks * 4);
+  L.hist = off;     off = align256(off + hist_bytes(n_units));
+  L.state = off;    off = align256(off + U * sizeof(UnitState));
+  L.wg_cnt = off;   off = align256(off + U * L.cand_wgs * 4);
+  L.cand = off;     off = align256(off + (U * L.cand_wgs << cs) * 4);
+  L.gran_gt = off;  off = align256(off + U * L.grans * 4);
+  L.gran_off = off; off = align256(off + U * L.grans * 4);
+  L.gran_eq = off;  off = align256(off + U * L.grans * 4);
   L.total = off;
   return L;
 }

@@ -123,13 +123,15 @@ def test_select_argument_errors():
     assert _select(kcnt=None) == ARG
     assert _select(kidx=None) == ARG
     assert _select(scores=A["scores"] + 2) == ARG
+    assert _select(maxr=(1 << 27) + 1, R=(1 << 27) + 1, U=1) == UNSUP  # beyond the select's unit size
     assert _select(flags=1) == WS  # no workspace
     assert _select(flags=0) == WS
     n = ctypes.c_size_t(1)
     assert _select(flags=1, wsb=ctypes.byref(n)) == OK
     size = n.value
-    # histograms, unit states, per-chunk offsets and tie counts (32 chunks of 1024 rows)
-    assert size == 8 * 4096 * 4 + 256 + 2 * 1024
+    # histograms, unit states (32 bytes each), candidate counts of 32 workgroups of 1024 rows,
+    # one candidate word per row, and three words per granule of 64 rows (512 per unit)
+    assert size == 8 * 4096 * 4 + 8 * 32 + 8 * 32 * 4 + 8 * 32768 * 4 + 3 * 8 * 512 * 4
     n2 = ctypes.c_size_t(0)
     assert _select(flags=0, wsb=ctypes.byref(n2)) == OK and n2.value == size
     ok = ctypes.c_size_t(size)
