@@ -25,10 +25,11 @@
 //                  (Resolving in the candidate kernel's last workgroup per unit would need an
 //                  agent-scope release in every workgroup, an L2 writeback each, which costs far
 //                  more here than the kernel boundary.)
-//  emit_kernel     one wave per granule (64 rows unless units are very long): writes each kept
-//                  row's index at  offset(granule) + (rows kept before it in the granule)  and,
-//                  when fused, copies the kept K/V rows and positions; every wave moves at most
-//                  64 rows per step, with all of a step's loads in flight at once.
+//  emit_kernel     one wave per granule (64 rows unless units are very long) writes each kept
+//                  row's index at  offset(granule) + (rows kept before it in the granule). When
+//                  fused, a granule has a second wave: the first copies the kept K rows and the
+//                  positions, the second the V rows, each with all of a step's loads in flight at
+//                  once (a dense run of kept rows is spread over many waves, not one CU).
 #include "tri_device.h"
 
 namespace tri {
@@ -223,21 +224,33 @@ __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a) {
 constexpr int kRN = 1024;
 constexpr int kRW = kRN / 64;
 constexpr int kRPer = kMaxGran / kRN;  // granules (and candidate workgroups) per thread
+constexpr int kPre = 8;                // candidates each thread loads with the first loads
+constexpr int kTieList = 1024;         // candidates whose top 22 bits are T's, kept in a list
 static_assert(kRPer * kRN == kMaxGran, "granules per thread");
+static_assert(kPre * (kRN / 8) <= (1 << kCandRowsShift), "preload stays inside a workgroup region");
 
 struct ResShared {
   uint32_t sh[4 * kRW];
   uint32_t found[2];
-  uint32_t cand[kCandCap];  // packed candidates: low 20 key bits << 12 | granule
-  uint32_t rhist[2][1024];  // radix bins of digits 2 and 3
-  union {
-    uint32_t wgoff[kMaxGran + 1];  // first candidate of each candidate workgroup
-    uint32_t cnt[kMaxGran];        // per granule: candidates above T (low 16 bits), equal (high 16)
-  } x;
+  uint32_t nlist;
+  uint32_t cand[kCandCap];         // packed candidates: low 20 key bits << 12 | granule
+  uint32_t rhist[2][1024];         // radix bins of digits 2 and 3
+  uint32_t wgoff[kMaxGran + 1];    // first candidate of each candidate workgroup
+  uint32_t cnt[kMaxGran];          // per granule: candidates above T (low 16 bits), equal (high 16)
+  uint32_t list[kTieList];         // candidates sharing T's digits 1 and 2
 };
+
+// Digit-3 bin, granule and "above" tests of a packed candidate: bits 31..22 are digit 2, bits
+// 21..12 digit 3, bits 11..0 the granule.
+__device__ __forceinline__ uint32_t cand_d2(uint32_t p) { return p >> 22; }
+__device__ __forceinline__ uint32_t cand_d3(uint32_t p) { return (p >> 12) & 1023u; }
 
 // One workgroup per unit: digits 2 and 3 of T among the candidates, then per-granule output
 // offsets and counts of ties before each granule. Leaves the unit's histogram at zero.
+// The candidates are loaded with the first loads (each of the unit's candidate workgroups gets
+// 1024/nwg threads that load kPre of its candidates each; more are fetched afterwards), placed
+// in LDS behind their workgroup's prefix and counted by digit 2 as they are placed; the digit-3
+// pass also counts, per granule, the candidates whose digit 2 is above T's.
 __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
   __shared__ ResShared L;
   const int u = blockIdx.x;
@@ -259,8 +272,18 @@ __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
   const uint32_t ngu = ((n - 1) >> gshift) + 1;  // granules of this unit
   const uint32_t nwg = ((n - 1) >> cshift) + 1;  // candidate workgroups of this unit
   const float* s = a.scores + ur.beg;
+  const uint32_t* cin = w.cand + (((size_t)u * WPU) << cshift);
 
-  // loads: this thread's granules and candidate workgroups 4t..4t+3
+  // loads: this thread's granules and candidate workgroups 4t..4t+3, and its share of the
+  // candidates of workgroup cw = t / tpw (entries ci + k*tpw, inside the region whatever the count)
+  uint32_t lg = 0;
+  while ((1u << lg) < nwg) ++lg;
+  const uint32_t tpw = lg > 10 ? 0u : ((kRN >> lg) < kRN / 8 ? (kRN >> lg) : kRN / 8);  // threads per workgroup
+  const uint32_t cw = tpw ? threadIdx.x / tpw : 0u, ci = tpw ? threadIdx.x % tpw : 0u;
+  const bool pre_ok = tpw != 0 && cw < nwg;
+  uint32_t pv[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) pv[k] = pre_ok ? cin[((size_t)cw << cshift) + ci + k * tpw] : 0u;
   uint32_t ggt[kRPer], wc[kRPer];
 #pragma unroll
   for (int q = 0; q < kRPer; ++q) {
@@ -270,88 +293,128 @@ __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
   }
   L.rhist[0][threadIdx.x] = 0u;
   L.rhist[1][threadIdx.x] = 0u;
+#pragma unroll
+  for (int q = 0; q < kRPer; ++q) L.cnt[kRPer * threadIdx.x + q] = 0u;
+  if (threadIdx.x == 0) L.nlist = 0u;
 
-  uint32_t wsum = 0;
-#pragma unroll
-  for (int q = 0; q < kRPer; ++q) wsum += wc[q];
   uint32_t nc;
-  uint32_t wex = dev::block_excl_scan_dpp<kRN>(wsum, L.sh, &nc);
+  uint32_t wex = dev::block_excl_scan_dpp<kRN>(wc[0] + wc[1] + wc[2] + wc[3], L.sh, &nc);
   const bool in_lds = nc <= (uint32_t)kCandCap;
-  if (in_lds) {
 #pragma unroll
-    for (int q = 0; q < kRPer; ++q) {
-      const uint32_t i = kRPer * threadIdx.x + q;
-      if (i < nwg) L.x.wgoff[i] = wex;
-      wex += wc[q];
-    }
-    if (threadIdx.x == 0) L.x.wgoff[nwg] = nc;
+  for (int q = 0; q < kRPer; ++q) {
+    const uint32_t i = kRPer * threadIdx.x + q;
+    if (i < nwg) L.wgoff[i] = wex;
+    wex += wc[q];
   }
+  if (threadIdx.x == 0) L.wgoff[nwg] = nc;
   __syncthreads();
+
+  uint32_t r = m - above0;
+  uint32_t pre, T, need;
   if (in_lds) {
-    // candidate j lives in the workgroup c with wgoff[c] <= j < wgoff[c + 1]
-    const uint32_t* cin = w.cand + (((size_t)u * WPU) << cshift);
-    for (uint32_t j0 = 0; j0 < nc; j0 += 2 * kRN) {
-      uint32_t v[2];
+    // ---- place the candidates, counting digit 2
+    if (pre_ok) {
+      const uint32_t base = L.wgoff[cw], cnt_w = L.wgoff[cw + 1] - base;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t j = j0 + h * kRN + threadIdx.x;
-        uint32_t lo = 0, hi = nwg;
-        while (hi - lo > 1) {
-          const uint32_t mid = (lo + hi) >> 1;
-          if (L.x.wgoff[mid] <= j) lo = mid; else hi = mid;
+      for (int k = 0; k < kPre; ++k) {
+        const uint32_t i = ci + k * tpw;
+        if (i < cnt_w) {
+          L.cand[base + i] = pv[k];
+          atomicAdd(&L.rhist[0][cand_d2(pv[k])], 1u);
         }
-        v[h] = j < nc ? cin[((size_t)lo << cshift) + (j - L.x.wgoff[lo])] : 0u;
       }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t j = j0 + h * kRN + threadIdx.x;
-        if (j < nc) L.cand[j] = v[h];
+    }
+    // candidates past the preloaded share: the same threads go on; with more than 1024
+    // candidate workgroups, one thread per workgroup takes all of them
+    if (tpw) {
+      if (cw < nwg) {
+        const uint32_t base = L.wgoff[cw], cnt_w = L.wgoff[cw + 1] - base;
+        for (uint32_t i = tpw * kPre + ci; i < cnt_w; i += tpw) {
+          const uint32_t v = cin[((size_t)cw << cshift) + i];
+          L.cand[base + i] = v;
+          atomicAdd(&L.rhist[0][cand_d2(v)], 1u);
+        }
+      }
+    } else {
+      for (uint32_t c = threadIdx.x; c < nwg; c += kRN) {
+        const uint32_t base = L.wgoff[c], cnt_w = L.wgoff[c + 1] - base;
+        for (uint32_t i = 0; i < cnt_w; ++i) {
+          const uint32_t v = cin[((size_t)c << cshift) + i];
+          L.cand[base + i] = v;
+          atomicAdd(&L.rhist[0][cand_d2(v)], 1u);
+        }
       }
     }
     __syncthreads();
-  }
-
-  // ---- digits 2 and 3 among the candidates (or, if they overflowed, among the scores)
-  uint32_t r = m - above0, pre = b0;
-#pragma unroll
-  for (int digit = 0; digit < 2; ++digit) {
-    const int sh = digit == 0 ? 10 : 0;
-    uint32_t* rh = L.rhist[digit];
-    if (in_lds) {
-      for (uint32_t j = threadIdx.x; j < nc; j += kRN) {
-        const uint32_t kk = (b0 << kHistShift) | (L.cand[j] >> 12);
-        if ((kk >> (sh + 10)) == pre) atomicAdd(&rh[(kk >> sh) & 1023u], 1u);
+    // ---- digit 2
+    uint32_t above;
+    {
+      const uint32_t v[1] = {L.rhist[0][1023 - threadIdx.x]};
+      const uint32_t d2 = block_find<kRN, 1>(v, 1024, r, L.sh, L.found, &above);
+      r -= above;
+      pre = (b0 << 10) | d2;
+    }
+    // ---- digit 3 among the candidates with T's digit 2; the others above it are counted per
+    // granule now
+    const uint32_t d2 = pre & 1023u;
+    for (uint32_t j = threadIdx.x; j < nc; j += kRN) {
+      const uint32_t p = L.cand[j];
+      const uint32_t dj = cand_d2(p);
+      if (dj > d2) {
+        atomicAdd(&L.cnt[p & 0xFFFu], 1u);
+      } else if (dj == d2) {
+        atomicAdd(&L.rhist[1][cand_d3(p)], 1u);
+        const uint32_t slot = atomicAdd(&L.nlist, 1u);
+        if (slot < (uint32_t)kTieList) L.list[slot] = p;
+      }
+    }
+    __syncthreads();
+    {
+      const uint32_t v[1] = {L.rhist[1][1023 - threadIdx.x]};
+      const uint32_t d3 = block_find<kRN, 1>(v, 1024, r, L.sh, L.found, &above);
+      r -= above;
+      pre = (pre << 10) | d3;
+    }
+    T = pre;
+    need = r;
+    // ---- the candidates with T's digit 2: above T or equal to it, per granule
+    const uint32_t d3 = T & 1023u;
+    const uint32_t nl = L.nlist;
+    if (nl <= (uint32_t)kTieList) {
+      for (uint32_t j = threadIdx.x; j < nl; j += kRN) {
+        const uint32_t p = L.list[j];
+        if (cand_d3(p) >= d3) atomicAdd(&L.cnt[p & 0xFFFu], cand_d3(p) > d3 ? 1u : 0x10000u);
       }
     } else {
+      for (uint32_t j = threadIdx.x; j < nc; j += kRN) {
+        const uint32_t p = L.cand[j];
+        if (cand_d2(p) == d2 && cand_d3(p) >= d3) atomicAdd(&L.cnt[p & 0xFFFu], cand_d3(p) > d3 ? 1u : 0x10000u);
+      }
+    }
+  } else {
+    // ---- more candidates than LDS holds: digits 2 and 3 and the per-granule counts from the
+    // scores themselves
+    pre = b0;
+#pragma unroll
+    for (int digit = 0; digit < 2; ++digit) {
+      const int sh = digit == 0 ? 10 : 0;
+      uint32_t* rh = L.rhist[digit];
       for (uint32_t i = threadIdx.x; i < n; i += kRN) {
         const uint32_t kk = order_key(load_at(s, i));
         if ((kk >> (sh + 10)) == pre) atomicAdd(&rh[(kk >> sh) & 1023u], 1u);
       }
+      __syncthreads();
+      const uint32_t v[1] = {rh[1023 - threadIdx.x]};
+      uint32_t above;
+      const uint32_t b = block_find<kRN, 1>(v, 1024, r, L.sh, L.found, &above);
+      r -= above;
+      pre = (pre << 10) | b;
     }
-    __syncthreads();
-    const uint32_t v[1] = {rh[1023 - threadIdx.x]};
-    uint32_t above;
-    const uint32_t b = block_find<kRN, 1>(v, 1024, r, L.sh, L.found, &above);
-    r -= above;
-    pre = (pre << 10) | b;
-  }
-  const uint32_t T = pre, need = r;
-
-  // ---- per granule: candidates above T and equal to T (the staged candidates are done with
-  // the workgroup offsets: the finds above end with a barrier)
-#pragma unroll
-  for (int q = 0; q < kRPer; ++q) L.x.cnt[kRPer * threadIdx.x + q] = 0u;
-  __syncthreads();
-  if (in_lds) {
-    for (uint32_t j = threadIdx.x; j < nc; j += kRN) {
-      const uint32_t p = L.cand[j];
-      const uint32_t kk = (b0 << kHistShift) | (p >> 12);
-      if (kk >= T) atomicAdd(&L.x.cnt[p & 0xFFFu], kk > T ? 1u : 0x10000u);
-    }
-  } else {
+    T = pre;
+    need = r;
     for (uint32_t i = threadIdx.x; i < n; i += kRN) {
       const uint32_t kk = order_key(load_at(s, i));
-      if ((kk >> kHistShift) == b0 && kk >= T) atomicAdd(&L.x.cnt[i >> gshift], kk > T ? 1u : 0x10000u);
+      if ((kk >> kHistShift) == b0 && kk >= T) atomicAdd(&L.cnt[i >> gshift], kk > T ? 1u : 0x10000u);
     }
   }
   __syncthreads();
@@ -362,7 +425,7 @@ __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
 #pragma unroll
   for (int q = 0; q < kRPer; ++q) {
     const uint32_t i = kRPer * threadIdx.x + q;
-    const uint32_t cc = i < ngu ? L.x.cnt[i] : 0u;
+    const uint32_t cc = i < ngu ? L.cnt[i] : 0u;
     e[q] = cc >> 16;
     kg[q] = ggt[q] + (cc & 0xFFFFu);
     se += e[q];
@@ -390,43 +453,35 @@ __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
 constexpr int kEN = 256;       // four waves, one granule each, no block-level synchronisation
 constexpr int kEW = kEN / 64;
 
-struct Piece {
-  uint4 k, v;
-};
-
-// Copy of one step's kept rows. Addresses are a wave-uniform base (the step's first row, the
-// step's first output slot) plus a 32-bit byte offset below 64 rows * row bytes.
+// Copy of one step's kept rows of one tensor (K or V). Addresses are a wave-uniform base (the
+// step's first row, the step's first output slot) plus a 32-bit byte offset below 64 rows * row
+// bytes.
 template <int CPR>
-struct Gather {
+struct RowCopy {
   static constexpr int kShift = CPR == 8 ? 3 : CPR == 16 ? 4 : CPR == 32 ? 5 : 6;
   static constexpr uint32_t kRowBytes = CPR * 16;
-  const char* __restrict__ K;  // row t0 of the unit
-  const char* __restrict__ V;
-  char* __restrict__ Ko;       // output slot s0
-  char* __restrict__ Vo;
-  uint32_t rows;  // lane j < kc: (j-th kept row) - t0
-  uint32_t total, room;
+  const char* __restrict__ src;  // row t0 of the unit
+  char* __restrict__ dst;        // output slot s0
+  uint32_t rows;                 // lane j < kc: (j-th kept row) - t0
+  uint32_t total, room;          // pieces (kc * CPR); output slots left
 
   // piece q of the kept rows (q clamped to total - 1): row j = q / CPR, 16-byte part q % CPR.
   // Call with every lane active (the row index comes from lane j).
-  __device__ __forceinline__ Piece load(uint32_t q) const {
+  __device__ __forceinline__ uint4 load(uint32_t q) const {
     const uint32_t qc = q < total ? q : total - 1;
     const uint32_t rj = (uint32_t)__shfl((int)rows, (int)(qc >> kShift), 64);
-    const uint32_t o = rj * kRowBytes + (qc & (CPR - 1)) * 16u;
-    return Piece{*reinterpret_cast<const uint4*>(K + o), *reinterpret_cast<const uint4*>(V + o)};
+    return *reinterpret_cast<const uint4*>(src + rj * kRowBytes + (qc & (CPR - 1)) * 16u);
   }
-  __device__ __forceinline__ void store(uint32_t q, const Piece& p) const {
+  __device__ __forceinline__ void store(uint32_t q, const uint4& v) const {
     if (q >= total || (q >> kShift) >= room) return;
-    const uint32_t o = q * 16u;  // slot j = q / CPR, part q % CPR: (j * CPR + part) * 16
-    *reinterpret_cast<uint4*>(Ko + o) = p.k;
-    *reinterpret_cast<uint4*>(Vo + o) = p.v;
+    *reinterpret_cast<uint4*>(dst + q * 16u) = v;  // slot j = q / CPR, part q % CPR
   }
   // all pieces in batches of NB per lane: every load of a batch is issued before its stores
   template <int NB>
   __device__ __forceinline__ void run() const {
     const uint32_t lane = threadIdx.x & 63;
     for (uint32_t q0 = 0; q0 < total; q0 += NB * 64) {  // uniform trip count
-      Piece p[NB];
+      uint4 p[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) p[i] = load(q0 + i * 64 + lane);
 #pragma unroll
@@ -435,17 +490,25 @@ struct Gather {
   }
 };
 
+// With the gather, each granule has two waves that both scan it: the first writes the kept
+// indices and positions and copies the K rows, the second copies the V rows.
+template <int CPR>
+constexpr int waves_per_granule() { return CPR > 0 ? 2 : 1; }
+
 template <int CPR>  // 16-byte pieces per K/V row; 0: no gather
 __global__ __launch_bounds__(kEN) void emit_kernel(SelectArgs a) {
+  constexpr int WPG = waves_per_granule<CPR>();
+  constexpr int GPB = kEW / WPG;  // granules per workgroup
   const int NG = a.lay.grans, gshift = a.lay.gran_shift;
-  const int EPU = (NG + kEW - 1) / kEW;
+  const int EPU = (NG + GPB - 1) / GPB;
   const int u = blockIdx.x / EPU, c = blockIdx.x - u * EPU;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const bool second = WPG == 2 && (wave & 1);  // the V wave of its granule
   const WsPtrs w = ws_ptrs(a);
   const dev::UnitRows ur = dev::unit_rows(a.row_off, u, a.total_rows, a.max_rows);
   const uint32_t n = (uint32_t)ur.n;
-  const uint32_t g = (uint32_t)(c * kEW + wave);
+  const uint32_t g = (uint32_t)(c * GPB + wave / WPG);
   const uint32_t gc = g < (uint32_t)NG ? g : (uint32_t)NG - 1;
   const uint32_t i0 = g << gshift;
   const float* sc = a.scores + ur.beg;
@@ -494,27 +557,30 @@ __global__ __launch_bounds__(kEN) void emit_kernel(SelectArgs a) {
     const uint32_t dst = keep ? lanes_below(mk) : kc + lanes_below(~mk);
     const uint32_t rows = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)r);
     const uint32_t room = s0 < m ? m - s0 : 0u;  // slots left (all of them, with a consistent workspace)
-    if (lane < kc && lane < room) {
+    if (!second && lane < kc && lane < room) {
       out[s0 + lane] = (int32_t)rows;
       if (CPR > 0 && a.pos_out) a.pos_out[obase + s0 + lane] = a.pos[ur.beg + rows];
     }
     if constexpr (CPR > 0) {
       constexpr int64_t RB = CPR * 16;
-      const Gather<CPR> G{static_cast<const char*>(a.K) + (ur.beg + t0) * RB,
-                          static_cast<const char*>(a.V) + (ur.beg + t0) * RB,
-                          static_cast<char*>(a.K_out) + (obase + s0) * RB,
-                          static_cast<char*>(a.V_out) + (obase + s0) * RB, rows - t0, kc * CPR, room};
+      const RowCopy<CPR> cp{static_cast<const char*>(second ? a.V : a.K) + (ur.beg + t0) * RB,
+                            static_cast<char*>(second ? a.V_out : a.K_out) + (obase + s0) * RB, rows - t0,
+                            kc * CPR, room};
       // pieces per lane: kc * CPR / 64, at most CPR; a full step of 256-byte rows in one batch
-      if (G.total <= 4 * 64) G.template run<4>();
-      else if (G.total <= 8 * 64) G.template run<8>();
-      else G.template run<16>();
+      if (cp.total <= 4 * 64) cp.template run<4>();
+      else if (cp.total <= 8 * 64) cp.template run<8>();
+      else cp.template run<16>();
     }
   }
 }
 
 template <int CPR>
-void launch_emit(const SelectArgs& a, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL(emit_kernel<CPR>, dim3(grid), dim3(kEN), 0, s, a);
+hipError_t launch_emit(const SelectArgs& a, hipStream_t s) {
+  constexpr int GPB = kEW / waves_per_granule<CPR>();
+  const int64_t grid = (int64_t)a.n_units * ((a.lay.grans + GPB - 1) / GPB);
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(emit_kernel<CPR>, dim3((unsigned)grid), dim3(kEN), 0, s, a);
+  return hipSuccess;
 }
 
 }  // namespace
@@ -522,24 +588,27 @@ void launch_emit(const SelectArgs& a, unsigned grid, hipStream_t s) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   const int64_t U = a.n_units;
   const int64_t cand_grid = U * a.lay.cand_wgs;
-  const int64_t emit_grid = U * ((a.lay.grans + kEW - 1) / kEW);
   const int64_t hpu = (a.max_rows + kHRows - 1) / kHRows;
-  if (cand_grid > 0x7FFFFFFF || emit_grid > 0x7FFFFFFF || U * hpu > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (cand_grid > 0x7FFFFFFF || U * hpu > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (U * ((a.lay.grans + kEW - 1) / kEW) * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;  // emit grids
+  if (a.K_out != nullptr && a.row_bytes != 128 && a.row_bytes != 256 && a.row_bytes != 512 && a.row_bytes != 1024)
+    return hipErrorInvalidValue;
   if (!a.hist_ready && hpu > 0)
     hipLaunchKernelGGL(hist_kernel, dim3((unsigned)(U * hpu)), dim3(kHN), 0, s, a, (int)hpu);
   hipLaunchKernelGGL(cand_kernel, dim3((unsigned)cand_grid), dim3(kCN), 0, s, a);
   hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)U), dim3(kRN), 0, s, a);
+  hipError_t e = hipSuccess;
   if (a.K_out == nullptr) {
-    launch_emit<0>(a, (unsigned)emit_grid, s);
+    e = launch_emit<0>(a, s);
   } else {
     switch (a.row_bytes / 16) {
-      case 8: launch_emit<8>(a, (unsigned)emit_grid, s); break;
-      case 16: launch_emit<16>(a, (unsigned)emit_grid, s); break;
-      case 32: launch_emit<32>(a, (unsigned)emit_grid, s); break;
-      case 64: launch_emit<64>(a, (unsigned)emit_grid, s); break;
-      default: return hipErrorInvalidValue;
+      case 8: e = launch_emit<8>(a, s); break;
+      case 16: e = launch_emit<16>(a, s); break;
+      case 32: e = launch_emit<32>(a, s); break;
+      default: e = launch_emit<64>(a, s); break;
     }
   }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -94,6 +94,28 @@ def widen(keys, dtype):
     return O.widen_bf16(keys) if dtype == "bf16" else np.asarray(keys, dtype=np.float32).astype(np.float64)
 
 
+def order_keys(scores):
+    """Monotone u32 keys of binary32 scores (-0 == +0, NaN lowest), as the select compares them."""
+    b = np.asarray(scores, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    mag = b & 0x7FFFFFFF
+    k = np.where(b & 0x80000000, (~b) & 0xFFFFFFFF, b | 0x80000000)
+    k = np.where(mag == 0, 0x80000000, k)
+    k = np.where(mag > 0x7F800000, 0, k)
+    return k.astype(np.uint64)
+
+
+def candidate_profile(scores, B, rows_per_group=1024):
+    """Select-path facts for one unit's scores: the number of keys sharing the B-th key's top 12
+    bits (candidates), the largest number of them in one group of rows, and the number sharing
+    its top 22 bits. Used to show that a test reaches the code path it is meant for."""
+    k = order_keys(scores)
+    m = min(B, k.size)
+    T = np.sort(k)[::-1][m - 1]
+    cand = (k >> 20) == (T >> 20)
+    per = np.add.reduceat(cand.astype(np.int64), np.arange(0, k.size, rows_per_group))
+    return int(cand.sum()), int(per.max()), int(np.sum((k >> 10) == (T >> 10)))
+
+
 def oracle_unit(P, i, wl, theta=None, offsets=None, centers=None, layout="interleaved"):
     """fp64 reference scores of unit i and the per-key tolerance scale L1_k / F."""
     theta = wl.theta if theta is None else theta

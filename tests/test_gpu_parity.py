@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 from synthgen import pack_units, workload
-from tests._parity import TOL, check_unit, gen_workers, oracle_unit, run_gpu, score_error
+from tests._parity import TOL, candidate_profile, check_unit, gen_workers, oracle_unit, run_gpu, score_error
 
 pytestmark = pytest.mark.gpu
 
@@ -153,6 +153,49 @@ def test_quantized_scores_heavy_ties():
         out = run_gpu(P, wl, 3000, path=path)
         for i in range(2):
             check_unit(P, i, wl, out, 3000, label=f"quantized {path}")
+
+
+def test_dense_candidate_workgroup():
+    """1100 rows of one unit share one key and one position, so their scores tie exactly, and the
+    budget puts the threshold inside that group: one candidate workgroup holds many more
+    candidates than the resolve kernel preloads per workgroup, and the tie group is longer than
+    its tie list."""
+    wl = dataclasses.replace(workload("c2"), heads=1)
+    P = pack_units(wl, [0], [20000])
+    P["keys"][5000:6100] = P["keys"][5000]
+    P["pos"][5000:6100] = P["pos"][5000]
+    s_ref, scale = oracle_unit(P, 0, wl)
+    above = int(np.sum(s_ref > s_ref[5000]))
+    say(f"case dense candidate workgroup ({above} rows above the tie group)")
+    for extra in [1, 550, 1100]:
+        B = above + extra
+        out = run_gpu(P, wl, B)
+        check_unit(P, 0, wl, out, B, s_ref=s_ref, scale=scale, label=f"dense-cand +{extra}")
+        nc, per_group, tie22 = candidate_profile(out["scores"], B)
+        if extra < 1100:  # the threshold is the tie group's score
+            assert nc <= 4096 and per_group > 256 and tie22 > 1024, (nc, per_group, tie22)
+        kept = set(out["kept_idx"][0, :B].tolist())
+        tied = [r for r in range(5000, 6100) if r in kept]
+        assert tied == list(range(5000, 5000 + len(tied))), "ties keep the lowest rows"
+
+
+def test_very_long_unit():
+    """One unit of 1.1 M rows: more than 1024 candidate workgroups and 512-row granules (eight
+    emit steps per wave), with small and large budgets."""
+    wl = dataclasses.replace(workload("c2"), heads=1)
+    n = 1_100_000
+    say("case very long unit (generating)")
+    P = pack_units(wl, [0], [n])
+    s_ref, scale = oracle_unit(P, 0, wl)
+    for B in [100, 5000, 200000]:
+        say(f"case very long unit B={B}")
+        out = run_gpu(P, wl, B)
+        check_unit(P, 0, wl, out, B, s_ref=s_ref, scale=scale, label=f"long B={B}")
+        assert out["ws_after"]
+        nc, _, _ = candidate_profile(out["scores"], B)
+        say(f"   candidates {nc}")
+        if B == 100:  # staged in LDS, one thread per candidate workgroup
+            assert nc <= 4096, nc
 
 
 def test_half_split_layout_matches_interleaved():
