@@ -211,6 +211,32 @@ def main():
     del splans, ws_score
     k_score = e2.elapsed_time(e3) * 1e3 / args.steps
 
+    # the same pass with the keys read as stored after the rotary rotation (TRI_KEYS_ROTATED):
+    # one coefficient vector per unit, no positions and no trigonometry per key. The key bits
+    # are the same copies (their values do not change the work).
+    rot = tri.TRI_BANDS_INTERLEAVED | tri.TRI_KEYS_ROTATED
+    rplans = [tri.PassPlan(c["K"], c["V"], c["pos"], c["row_off"], max_rows, c["t"], c["mu"], wl.theta, B,
+                           ws=c["ws"], scores=c["scores"], kept_idx=c["kept_idx"], kept_cnt=c["kept_cnt"],
+                           K_out=c["K_out"], V_out=c["V_out"], pos_out=c["pos_out"], layout=rot)
+              for c in copies]
+    ws_rs = tri.make_workspace(U, max_rows, dev)
+    rsplans = [tri.ScorePlan(c["K"], c["row_off"], max_rows, None, c["t"], c["mu"], wl.theta,
+                             scores=c["scores"], ws=ws_rs, layout=rot) for c in copies]
+    rot_times = []
+    for plist in (rplans, rsplans):
+        for i in range(args.warmup):
+            plist[i % len(plist)].run()
+        torch.cuda.synchronize()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
+        for i in range(args.steps):
+            plist[i % len(plist)].run()
+        eb.record()
+        torch.cuda.synchronize()
+        rot_times.append(ea.elapsed_time(eb) * 1e3 / args.steps)
+    del rplans, rsplans, ws_rs
+    rot_pass_us, rot_score_us = rot_times
+
     alg = algorithmic_bytes(wl, R, U)
     alg_total = sum(alg.values())
     secs = ms * 1e-3
@@ -256,6 +282,13 @@ def main():
             "algorithmic_bytes_per_launch": score_bytes,
         },
         "kernel_source_sha256_16": khash,
+        "rotated_keys": {
+            "note": "same workload, keys read as stored after the rotary rotation",
+            "us_per_pass": rot_pass_us,
+            "keys_per_s": R / (rot_pass_us * 1e-6),
+            "score_kernel_us": rot_score_us,
+            "score_kernel_gbps": alg["K"] / (rot_score_us * 1e-6) / 1e9,
+        },
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, P, B, args.cpu_seconds)

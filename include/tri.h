@@ -58,6 +58,9 @@ extern "C" {
 /* how the d coordinates of a key pair up into F complex bands */
 #define TRI_BANDS_INTERLEAVED 0  /* band f = (x[2f], x[2f+1]) */
 #define TRI_BANDS_HALF_SPLIT  1  /* band f = (x[f], x[f + d/2]) (rotate-half storage) */
+/* OR-ed into a layout: the keys are stored after the rotary rotation at their own positions,
+ * band f holding k_f * e^{i omega_f pos} (see tri_score) */
+#define TRI_KEYS_ROTATED 0x100
 
 /* flags of tri_select_topb */
 #define TRI_SELECT_HIST_FROM_SCORE 1u  /* ws holds the histogram tri_score accumulated */
@@ -104,14 +107,15 @@ int tri_fold_weights(int d, double theta, const int64_t* offsets, int n_offsets,
  *   keys        device, [total_rows][d] elements of `dtype`, rows of unit u at
  *               row_off[u] .. row_off[u+1]-1
  *   dtype       TRI_DT_BF16 or TRI_DT_F32
- *   layout      TRI_BANDS_INTERLEAVED or TRI_BANDS_HALF_SPLIT
+ *   layout      TRI_BANDS_INTERLEAVED or TRI_BANDS_HALF_SPLIT, optionally | TRI_KEYS_ROTATED
  *   d           64, 128 or 256
  *   theta       rotary base (> 0, finite); the kernel derives omega_f from it
  *   row_off     device int64[n_units+1]: 0 = row_off[0] <= row_off[1] <= ... = total_rows
  *   n_units     >= 1
  *   total_rows  host copy of row_off[n_units] (>= 0)
  *   max_rows    host bound on every N_u (>= 0); rows of a unit beyond it are not scored
- *   pos         device int32[total_rows]: position of each key
+ *   pos         device int32[total_rows]: position of each key (not read, and may be NULL,
+ *               with TRI_KEYS_ROTATED)
  *   t_now       device int32[n_units]: current position of each unit
  *   mu          device float[n_units][F][2]: mu' (tri_fold_weights' mu_out)
  *   scores      device float[total_rows]: output (binary32); must not overlap the inputs
@@ -128,9 +132,17 @@ int tri_fold_weights(int d, double theta, const int64_t* offsets, int n_offsets,
  *                                 scores into it, and tri_select_topb called with
  *                                 TRI_SELECT_HIST_FROM_SCORE and the same ws consumes it and
  *                                 returns ws to its rest state.
- * Device preconditions: 0 <= t_u - pos[r] < 2^24; finite keys and mu'.
+ * Rotated keys (TRI_KEYS_ROTATED): a serving cache that stores keys after the rotary
+ *   embedding holds krot_{r,f} = k_{r,f} e^{i omega_f pos[r]}. Rotations compose by adding
+ *   angles ([N] "The same score, read as arrows in the plane"), so the same score is
+ *       score[r] = Re{ sum_f (mu'_{u,f} e^{i omega_f t_u}) * conj(krot_{r,f}) },
+ *   a dot product of each key with one coefficient vector per unit: positions are not read
+ *   and no trigonometry is evaluated per key.
+ * Device preconditions: 0 <= t_u - pos[r] < 2^24 (rotated keys: 0 <= t_u < 2^24); finite keys
+ *   and mu'.
  * Precision: rotation phase in 23-bit fixed point plus a binary32 residual, hardware
- *   sine/cosine, binary32 accumulation; mu' enters as a two-term bfloat16 split for bf16 keys.
+ *   sine/cosine, binary32 accumulation; mu' (with rotated keys, mu' e^{i omega t}) enters as a
+ *   two-term bfloat16 split for bf16 keys.
  */
 int tri_score(const void* keys, int dtype, int layout, int d, double theta,
               const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,

@@ -11,6 +11,7 @@ from ._abi import (  # noqa: F401
     TRI_BANDS_INTERLEAVED,
     TRI_DT_BF16,
     TRI_DT_F32,
+    TRI_KEYS_ROTATED,
     TRI_SELECT_HIST_FROM_SCORE,
     PassPlan,
     ScorePlan,

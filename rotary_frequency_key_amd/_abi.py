@@ -15,6 +15,7 @@ TRI_DT_F32 = 0
 TRI_DT_BF16 = 1
 TRI_BANDS_INTERLEAVED = 0
 TRI_BANDS_HALF_SPLIT = 1
+TRI_KEYS_ROTATED = 0x100  # OR into a layout: keys stored after the rotary rotation
 TRI_SELECT_HIST_FROM_SCORE = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -138,20 +139,24 @@ def make_workspace(n_units: int, max_rows: int, device) -> torch.Tensor:
     return torch.zeros(workspace_bytes(n_units, max_rows), dtype=torch.uint8, device=device)
 
 
-def tri_score(keys: torch.Tensor, row_off: torch.Tensor, max_rows: int, pos: torch.Tensor,
+def tri_score(keys: torch.Tensor, row_off: torch.Tensor, max_rows: int, pos: Optional[torch.Tensor],
               t_now: torch.Tensor, mu: torch.Tensor, theta: float, *,
               layout: int = TRI_BANDS_INTERLEAVED, scores: Optional[torch.Tensor] = None,
               ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Scores of every key; pos may be None when layout includes TRI_KEYS_ROTATED."""
     _dev(keys, "keys", ndim=2)
     dt = _key_dtype(keys)
     R, d = keys.shape
     _dev(row_off, "row_off", torch.int64, 1)
     U = row_off.numel() - 1
-    _dev(pos, "pos", torch.int32, 1)
+    if pos is not None or not (layout & TRI_KEYS_ROTATED):
+        _dev(pos, "pos", torch.int32, 1)
+        if pos.numel() != R:
+            raise ValueError("pos has the wrong size")
     _dev(t_now, "t_now", torch.int32, 1)
     _dev(mu, "mu", torch.float32)
-    if pos.numel() != R or t_now.numel() != U or mu.numel() != U * d:
-        raise ValueError("pos, t_now or mu has the wrong size")
+    if t_now.numel() != U or mu.numel() != U * d:
+        raise ValueError("t_now or mu has the wrong size")
     if scores is None:
         scores = torch.empty(R, dtype=torch.float32, device=keys.device)
     _dev(scores, "scores", torch.float32, 1)
@@ -318,12 +323,15 @@ class ScorePlan:
         R, d = keys.shape
         _dev(row_off, "row_off", torch.int64, 1)
         U = row_off.numel() - 1
-        _dev(pos, "pos", torch.int32, 1)
+        if pos is not None or not (layout & TRI_KEYS_ROTATED):
+            _dev(pos, "pos", torch.int32, 1)
+            if pos.numel() != R:
+                raise ValueError("pos has the wrong size")
         _dev(t_now, "t_now", torch.int32, 1)
         _dev(mu, "mu", torch.float32)
         _dev(scores, "scores", torch.float32, 1)
-        if pos.numel() != R or t_now.numel() != U or mu.numel() != U * d or scores.numel() != R:
-            raise ValueError("pos, t_now, mu or scores has the wrong size")
+        if t_now.numel() != U or mu.numel() != U * d or scores.numel() != R:
+            raise ValueError("t_now, mu or scores has the wrong size")
         wsp, self._nbytes = None, None
         if ws is not None:
             _dev(ws, "ws", torch.uint8, 1)

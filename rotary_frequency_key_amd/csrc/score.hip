@@ -154,6 +154,10 @@ struct CenterCoef<kDtBf16> {
     x = dot2(k.b[j], xh[j], dot2_z(k.b[j], xl[j]));
     y = dot2(k.b[j], yh[j], dot2_z(k.b[j], yl[j]));
   }
+  template <class T>
+  __device__ __forceinline__ float x(const T& k, int j) const {
+    return dot2(k.b[j], xh[j], dot2_z(k.b[j], xl[j]));
+  }
 };
 
 template <>
@@ -168,6 +172,10 @@ struct CenterCoef<kDtF32> {
     x = fmaf(a[j], k.re[j], b[j] * k.im[j]);
     y = fmaf(b[j], k.re[j], -(a[j] * k.im[j]));
   }
+  template <class T>
+  __device__ __forceinline__ float x(const T& k, int j) const {
+    return fmaf(a[j], k.re[j], b[j] * k.im[j]);
+  }
 };
 
 constexpr int kScoreThreads = 256;
@@ -176,7 +184,20 @@ constexpr int kRowsPerLoad = 8;  // rows per lane group in flight per iteration
 template <int D>
 constexpr int score_rows_per_block() { return 512; }
 
-template <int DT, int LAYOUT, int D, bool HIST>
+// The rotation phase of band j at distance dl, in revolutions (+1, which sine and cosine in
+// revolutions ignore): ((dl * step) mod 2^23) / 2^23 + dl * resid, for dl < 2^24.
+__device__ __forceinline__ float band_phase(uint32_t dl, float df, uint32_t step, float resid) {
+  const uint32_t prod = mul_u24(dl, step);
+  const float one_frac = __uint_as_float((prod & 0x7FFFFFu) | 0x3F800000u);
+  return fmaf(df, resid, one_frac);
+}
+
+// ROT: the keys were rotated at their own positions (stored after the rotary embedding). Then
+// conj(k_f) e^{i omega_f (t - p)} = conj(k_f e^{i omega_f p}) e^{i omega_f t}, so the score is
+// Re{ sum_f (mu'_f e^{i omega_f t}) conj(krot_f) }: one coefficient vector per unit, a plain dot
+// product per key, no positions and no per-key trigonometry ("The same score, read as arrows in
+// the plane": the rotation is a multiplication, and rotations compose by adding angles).
+template <int DT, int LAYOUT, int D, bool HIST, bool ROT>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int chunks_per_unit, BandConst bc) {
   constexpr int F = D / 2;
   constexpr int LPR = F / 4;                 // lanes per row, 4 bands each
@@ -205,6 +226,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int c
   const int l = lane % LPR;   // lane within the row group: bands 4l .. 4l+3
   const int gw = lane / LPR;  // row group within the wave
 
+  // Rows are addressed relative to r0 with 32-bit offsets; rows past the end load the last
+  // row of the chunk instead (always valid) and are never stored.
+  const char* kbase = static_cast<const char*>(a.keys) + r0 * L::kRowBytes;
+  const int32_t* pbase = ROT ? nullptr : a.pos + r0;
+  const uint32_t last = (uint32_t)(r1 - r0 - 1);
+  const uint32_t wave_row = (uint32_t)(wave * ROWS_WAVE + gw);
+  KT kb[M];
+  int32_t pb[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint32_t row = min(wave_row + m * GPW, last);
+    kb[m] = L::load(kbase, row, l);
+    pb[m] = ROT ? 0 : pbase[row];
+  }
+
   if constexpr (HIST) {
     for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) lhist[i] = 0u;
   }
@@ -221,26 +257,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int c
 #pragma unroll
     for (int j = 0; j < 4; ++j) { step[j] = bc.step[4 * l + j] & 0x7FFFFFu; resid[j] = bc.resid[4 * l + j]; }
   }
-  CenterCoef<DT> cc;
-  cc.init(cre, cim);
   const int32_t t = a.t_now[unit];
+  CenterCoef<DT> cc;
+  if constexpr (ROT) {
+    // mu'_f e^{i omega_f t}
+    const uint32_t tl = (uint32_t)t;
+    const float tf = (float)tl;
+    float rre[4], rim[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float rev = band_phase(tl, tf, step[j], resid[j]);
+      const float sn = __builtin_amdgcn_sinf(rev);
+      const float cs = __builtin_amdgcn_cosf(rev);
+      rre[j] = fmaf(cre[j], cs, -(cim[j] * sn));
+      rim[j] = fmaf(cre[j], sn, cim[j] * cs);
+    }
+    cc.init(rre, rim);
+  } else {
+    cc.init(cre, cim);
+  }
 
   if constexpr (HIST) __syncthreads();
-
-  // Rows are addressed relative to r0 with 32-bit offsets; rows past the end load the last
-  // row of the chunk instead (always valid) and are never stored.
-  const char* kbase = static_cast<const char*>(a.keys) + r0 * L::kRowBytes;
-  const int32_t* pbase = a.pos + r0;
-  const uint32_t last = (uint32_t)(r1 - r0 - 1);
-  const uint32_t wave_row = (uint32_t)(wave * ROWS_WAVE + gw);
-  KT kb[M];
-  int32_t pb[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint32_t row = min(wave_row + m * GPW, last);
-    kb[m] = L::load(kbase, row, l);
-    pb[m] = pbase[row];
-  }
 
   for (int it = 0; it < ITERS; ++it) {
     KT kc[M];
@@ -253,26 +290,29 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int c
       for (int m = 0; m < M; ++m) {
         const uint32_t row = min(base + ROWS_ITER + m * GPW, last);
         kb[m] = L::load(kbase, row, l);
-        pb[m] = pbase[row];
+        pb[m] = ROT ? 0 : pbase[row];
       }
     }
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const uint32_t dl = (uint32_t)(t - pc[m]);
-      const float df = (float)dl;
       float s = 0.f;
+      if constexpr (ROT) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t prod = mul_u24(dl, step[j]);
-        const float one_frac = __uint_as_float((prod & 0x7FFFFFu) | 0x3F800000u);
-        const float rev = fmaf(df, resid[j], one_frac);  // revolutions (+1, harmless)
-        const float sn = __builtin_amdgcn_sinf(rev);
-        const float cs = __builtin_amdgcn_cosf(rev);
-        float x, y;
-        cc.xy(kc[m], j, x, y);
-        s = fmaf(x, cs, s);
-        s = fmaf(-y, sn, s);
+        for (int j = 0; j < 4; ++j) s += cc.x(kc[m], j);
+      } else {
+        const uint32_t dl = (uint32_t)(t - pc[m]);
+        const float df = (float)dl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float rev = band_phase(dl, df, step[j], resid[j]);
+          const float sn = __builtin_amdgcn_sinf(rev);
+          const float cs = __builtin_amdgcn_cosf(rev);
+          float x, y;
+          cc.xy(kc[m], j, x, y);
+          s = fmaf(x, cs, s);
+          s = fmaf(-y, sn, s);
+        }
       }
       acc[m] = group_sum<LPR>(s);
     }
@@ -310,12 +350,14 @@ hipError_t launch_score_t(const ScoreArgs& a, const BandConst& bc, hipStream_t s
   const int64_t grid = chunks * a.n_units;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (a.hist)
-    hipLaunchKernelGGL((score_kernel<DT, LAYOUT, D, true>), dim3((unsigned)grid), dim3(kScoreThreads), 0, s,
-                       a, (int)chunks, bc);
-  else
-    hipLaunchKernelGGL((score_kernel<DT, LAYOUT, D, false>), dim3((unsigned)grid), dim3(kScoreThreads), 0, s,
-                       a, (int)chunks, bc);
+  const dim3 g((unsigned)grid), b(kScoreThreads);
+  if (a.rotated) {
+    if (a.hist) hipLaunchKernelGGL((score_kernel<DT, LAYOUT, D, true, true>), g, b, 0, s, a, (int)chunks, bc);
+    else hipLaunchKernelGGL((score_kernel<DT, LAYOUT, D, false, true>), g, b, 0, s, a, (int)chunks, bc);
+  } else {
+    if (a.hist) hipLaunchKernelGGL((score_kernel<DT, LAYOUT, D, true, false>), g, b, 0, s, a, (int)chunks, bc);
+    else hipLaunchKernelGGL((score_kernel<DT, LAYOUT, D, false, false>), g, b, 0, s, a, (int)chunks, bc);
+  }
   return hipGetLastError();
 }
 

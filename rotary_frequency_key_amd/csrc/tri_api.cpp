@@ -53,14 +53,16 @@ int check_score(const void* keys, int dtype, int layout, int d, double theta, co
                 const float* mu, const float* scores, const void* hist, size_t hist_bytes) {
   if (n_units < 1 || total_rows < 0 || max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
   if (dtype != TRI_DT_F32 && dtype != TRI_DT_BF16) return TRI_ERR_ARG;
-  if (layout != TRI_BANDS_INTERLEAVED && layout != TRI_BANDS_HALF_SPLIT) return TRI_ERR_ARG;
+  const int bands = layout & ~TRI_KEYS_ROTATED;
+  const bool rotated = (layout & TRI_KEYS_ROTATED) != 0;
+  if (bands != TRI_BANDS_INTERLEAVED && bands != TRI_BANDS_HALF_SPLIT) return TRI_ERR_ARG;
   if (!finite_positive(theta)) return TRI_ERR_ARG;
   if (d < 2 || (d % 2) != 0) return TRI_ERR_ARG;
   if (d != 64 && d != 128 && d != 256) return TRI_ERR_UNSUPPORTED;
   if (row_off == nullptr || !aligned(row_off, 8)) return TRI_ERR_ARG;
   if (t_now == nullptr || mu == nullptr || !aligned(t_now, 4) || !aligned(mu, 16)) return TRI_ERR_ARG;
   if (total_rows > 0) {
-    if (keys == nullptr || pos == nullptr || scores == nullptr) return TRI_ERR_ARG;
+    if (keys == nullptr || scores == nullptr || (!rotated && pos == nullptr)) return TRI_ERR_ARG;
     if (!aligned(keys, 16) || !aligned(pos, 4) || !aligned(scores, 4)) return TRI_ERR_ARG;
   }
   if (hist != nullptr && !aligned(hist, 256)) return TRI_ERR_ARG;
@@ -133,8 +135,8 @@ hipError_t launch_score_call(const void* keys, int dtype, int layout, int d, dou
                              const int32_t* t_now, const float* mu, float* scores, void* hist, hipStream_t s) {
   tri::BandConst bc;
   band_constants(d, theta, &bc);
-  tri::ScoreArgs a{keys, dtype, layout, d, row_off, n_units, total_rows, max_rows,
-                   pos, t_now, mu, scores, static_cast<uint32_t*>(hist)};
+  tri::ScoreArgs a{keys, dtype, layout & ~TRI_KEYS_ROTATED, d, (layout & TRI_KEYS_ROTATED) != 0, row_off,
+                   n_units, total_rows, max_rows, pos, t_now, mu, scores, static_cast<uint32_t*>(hist)};
   return tri::launch_score(a, bc, s);
 }
 

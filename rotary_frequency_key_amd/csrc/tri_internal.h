@@ -88,7 +88,8 @@ inline WsLayout ws_layout(int n_units, int64_t max_rows) {
 
 struct ScoreArgs {
   const void* keys;
-  int dtype, layout, d;
+  int dtype, layout, d;  // layout: band pairing only (TRI_BANDS_*)
+  bool rotated;          // keys stored after the rotary rotation at their positions
   const int64_t* row_off;
   int n_units;
   int64_t total_rows, max_rows;

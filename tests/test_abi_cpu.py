@@ -92,6 +92,8 @@ def test_score_argument_errors():
     assert _score(maxr=1 << 31) == ARG
     assert _score(keys=A["keys"] + 8) == ARG  # misaligned
     assert _score(mu=A["mu"] + 4) == ARG
+    assert _score(layout=0x102) == ARG  # unknown band layout under the rotated-keys flag
+    assert _score(layout=0x200) == ARG  # unknown flag
     assert _score(keys=None) == ARG
     assert _score(row_off=None) == ARG
     # scores overlapping the keys / positions

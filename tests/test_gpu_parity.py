@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 from synthgen import pack_units, workload
-from tests._parity import TOL, candidate_profile, check_unit, gen_workers, oracle_unit, run_gpu, score_error
+from tests._parity import TOL, candidate_profile, check_unit, gen_workers, oracle_unit, run_gpu, score_error, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -196,6 +196,61 @@ def test_very_long_unit():
         say(f"   candidates {nc}")
         if B == 100:  # staged in LDS, one thread per candidate workgroup
             assert nc <= 4096, nc
+
+
+def _rotated_case(wl, units, lengths, layout):
+    """Generated keys rotated at their positions in fp64 and stored (rounded) in wl.dtype, with
+    the oracle's post-rotation scores of the stored keys."""
+    from synthgen import f32_to_bf16_bits
+
+    P = pack_units(wl, units, lengths)
+    omega = O.rotary_frequencies(wl.d, wl.theta)
+    D = O.power_of_two_offsets()
+    F = wl.d // 2
+    lay = "half_split" if layout & 1 else "interleaved"
+    stored = np.empty_like(P["keys"])
+    refs = []
+    for i in range(len(units)):
+        a, b = P["row_off"][i], P["row_off"][i + 1]
+        kb = O.as_bands(widen(P["keys"][a:b], wl.dtype))  # generated keys, interleaved bands
+        kr = O.rotate_keys(kb, P["pos"][a:b], omega)
+        x = np.empty((b - a, wl.d), dtype=np.float64)
+        if lay == "interleaved":
+            x[:, 0::2], x[:, 1::2] = kr.real, kr.imag
+        else:
+            x[:, :F], x[:, F:] = kr.real, kr.imag
+        x32 = x.astype(np.float32)
+        stored[a:b] = f32_to_bf16_bits(x32) if wl.dtype == "bf16" else x32
+        ks = O.as_bands(widen(stored[a:b], wl.dtype), lay)  # what the kernel reads
+        mu = O.folded_center(O.as_bands(P["centers"][i].astype(np.float64)), O.fold_weights(omega, D))
+        s_ref = O.score_post_rope(mu, ks, int(P["t"][i]), omega)
+        scale = np.sum(np.abs(mu)[None, :] * np.abs(ks), axis=1) / F
+        refs.append((s_ref, scale))
+    P["keys"] = stored
+    return P, refs
+
+
+@pytest.mark.parametrize("dtype,layout", [("bf16", 0), ("bf16", 1), ("f32", 0)])
+def test_rotated_keys(dtype, layout):
+    """Keys stored after the rotary rotation: the score from one coefficient vector per unit
+    (mu' e^{i omega t}) against the oracle's post-rotation form of the same stored keys; the
+    score alone, called without positions, gives the same bits."""
+    import rotary_frequency_key_amd as tri
+
+    wl = dataclasses.replace(workload("c2"), dtype=dtype, heads=3)
+    P, refs = _rotated_case(wl, [0, 1, 2], [5000, 1500, 33], layout)
+    say(f"case rotated keys {dtype} layout {layout}")
+    out = run_gpu(P, wl, 700, layout=layout | tri.TRI_KEYS_ROTATED)
+    for i in range(3):
+        s_ref, scale = refs[i]
+        check_unit(P, i, wl, out, 700, s_ref=s_ref, scale=scale, label=f"rotated {dtype} {layout}")
+    dev = torch.device("cuda:0")
+    from tests._parity import keys_to_device
+    alone = tri.tri_score(keys_to_device(P["keys"], dtype, dev), torch.from_numpy(P["row_off"]).to(dev),
+                          int(np.diff(P["row_off"]).max()), None, torch.from_numpy(P["t"]).to(dev),
+                          torch.from_numpy(out["mu"]).to(dev), wl.theta, layout=layout | tri.TRI_KEYS_ROTATED)
+    torch.cuda.synchronize()
+    assert np.array_equal(alone.cpu().numpy(), out["scores"])
 
 
 def test_half_split_layout_matches_interleaved():
