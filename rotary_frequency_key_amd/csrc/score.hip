@@ -178,8 +178,8 @@ struct CenterCoef<kDtF32> {
   }
 };
 
-constexpr int kScoreThreads = 256;
-constexpr int kRowsPerLoad = 8;  // rows per lane group in flight per iteration
+constexpr int kScoreThreads = 512;
+constexpr int kRowsPerLoad = 4;  // rows per lane group in flight per iteration
 
 template <int D>
 constexpr int score_rows_per_block() { return 512; }

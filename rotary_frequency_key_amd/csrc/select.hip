@@ -28,8 +28,8 @@
 //  emit_kernel     one wave per granule (64 rows unless units are very long) writes each kept
 //                  row's index at  offset(granule) + (rows kept before it in the granule). When
 //                  fused, a granule has a second wave: the first copies the kept K rows and the
-//                  positions, the second the V rows, each with all of a step's loads in flight at
-//                  once (a dense run of kept rows is spread over many waves, not one CU).
+//                  positions, the second the V rows, up to 8 loads of 16 bytes per lane in flight
+//                  (a dense run of kept rows is spread over many waves, not one CU).
 #include "tri_device.h"
 
 namespace tri {
@@ -566,10 +566,10 @@ __global__ __launch_bounds__(kEN) void emit_kernel(SelectArgs a) {
       const RowCopy<CPR> cp{static_cast<const char*>(second ? a.V : a.K) + (ur.beg + t0) * RB,
                             static_cast<char*>(second ? a.V_out : a.K_out) + (obase + s0) * RB, rows - t0,
                             kc * CPR, room};
-      // pieces per lane: kc * CPR / 64, at most CPR; a full step of 256-byte rows in one batch
+      // pieces per lane: kc * CPR / 64, at most CPR; batches of at most 8 keep the VGPRs (and
+      // so the waves resident per SIMD) where a full batch of 16 would not pay for itself
       if (cp.total <= 4 * 64) cp.template run<4>();
-      else if (cp.total <= 8 * 64) cp.template run<8>();
-      else cp.template run<16>();
+      else cp.template run<8>();
     }
   }
 }
