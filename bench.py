@@ -111,6 +111,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-copy", action="store_true")
+    ap.add_argument("--no-steady", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -290,9 +291,88 @@ def main():
             "score_kernel_gbps": alg["K"] / (rot_score_us * 1e-6) / 1e9,
         },
     }
+    # free the pass copies before the steady-state cache
+    del copies, plans
+    torch.cuda.empty_cache()
+    if not args.no_steady:
+        result["steady_state"] = steady_state(tri, torch, dev, args)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, P, B, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
+    """Chat steady state (the 64-layer x 8-head x 4-sequence shape, B = 12000): every unit holds
+    the B rows kept by earlier passes, at sparse positions below 131072, and a 1024-row prefill
+    chunk at the next positions; tri_prune_inplace prunes the 13024 rows back to B in place.
+
+    The cache is synthetic: base_units units are generated (keys around a center as in every
+    workload, B positions drawn without replacement from 0..131071, then 1024 new ones) and
+    tiled replicas times on the device, 2048 units in all. Before each timed pass a fresh chunk
+    is copied into rows B.. of every unit (untimed, events bracket the pass only)."""
+    from synthgen import unit_inputs, workload
+
+    wl = workload("c5")
+    B = wl.budget
+    C = B + chunk
+    t_now = 131072 + chunk
+    Ks, Vs, Ps, Cs, pool_k, pool_v = [], [], [], [], [], []
+    for u in range(base_units):
+        x = unit_inputs(wl, u, C + chunk)  # C rows for the cache, one more chunk for the pool
+        rng = np.random.default_rng([wl.seed, 0xC5, u])
+        old = np.sort(rng.choice(131072, size=B, replace=False)).astype(np.int32)
+        Ks.append(x["keys"][:C]); Vs.append(x["values"][:C]); Cs.append(x["center"])
+        Ps.append(np.concatenate([old, np.arange(131072, t_now, dtype=np.int32)]))
+        pool_k.append(x["keys"][C:]); pool_v.append(x["values"][C:])
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    U = base_units * replicas
+    K = dev16(np.stack(Ks)).repeat(replicas, 1, 1).reshape(U * C, wl.d)
+    V = dev16(np.stack(Vs)).repeat(replicas, 1, 1).reshape(U * C, wl.d)
+    pos = torch.from_numpy(np.stack(Ps)).to(dev).repeat(replicas, 1).reshape(U * C)
+    chunk_k = dev16(np.stack(pool_k)).repeat(replicas, 1, 1)
+    chunk_v = dev16(np.stack(pool_v)).repeat(replicas, 1, 1)
+    chunk_p = torch.arange(131072, t_now, dtype=torch.int32, device=dev).repeat(U, 1)
+    _, mu = tri.tri_fold_weights(wl.d, wl.theta, np.array([1 << j for j in range(17)]), np.stack(Cs))
+    mu = torch.from_numpy(mu).to(dev).repeat(replicas, 1, 1).contiguous()
+    row_off = torch.arange(0, (U + 1) * C, C, dtype=torch.int64, device=dev)
+    t = torch.full((U,), t_now, dtype=torch.int32, device=dev)
+    plan = tri.InplacePlan(K, V, pos, row_off, C, t, mu, wl.theta, B,
+                           ws=tri.make_inplace_workspace(U, C, B, dev),
+                           scores=torch.empty(U * C, dtype=torch.float32, device=dev),
+                           kept_cnt=torch.empty(U, dtype=torch.int32, device=dev))
+    K3, V3, P2 = K.view(U, C, wl.d), V.view(U, C, wl.d), pos.view(U, C)
+
+    def append():
+        K3[:, B:].copy_(chunk_k)
+        V3[:, B:].copy_(chunk_v)
+        P2[:, B:].copy_(chunk_p)
+
+    steps = max(3, min(args.steps, 20))
+    for _ in range(2):
+        append()
+        plan.run()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        append()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        plan.run()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+    rows = U * C
+    # algorithmic bytes: every key row and position read, each moved row's K, V and position
+    # read and written (at most one chunk per unit)
+    moved_max = U * chunk * (2 * wl.d * 2 + 4) * 2
+    return {"units": U, "rows_per_unit": C, "budget": B, "chunk": chunk, "us_per_pass": us,
+            "keys_per_s": rows / (us * 1e-6),
+            "algorithmic_gbps": (rows * (wl.d * 2 + 4) + moved_max) / (us * 1e-6) / 1e9,
+            "note": f"{base_units} generated units tiled {replicas}x; chunk copy untimed"}
 
 
 if __name__ == "__main__":

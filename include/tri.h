@@ -231,6 +231,37 @@ int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, d
                    int32_t* kept_idx, int32_t* kept_cnt, void* K_out, void* V_out, int32_t* pos_out,
                    void* ws, size_t* ws_bytes, void* stream);
 
+/*
+ * tri_prune_inplace - the pruning pass on a cache that is pruned where it lives: the steady
+ * state of [R] chat serving, where every prefill chunk (1024 tokens with
+ * --max-num-batched-tokens 1024) appended to a cache of B kept rows triggers compression back
+ * to B (budget 12000 for chat).
+ *
+ * Scores and selects exactly as tri_prune_pass (same order, ties and counts). Instead of copying
+ * the kept rows out, it moves the fewest rows so that unit u's kept rows occupy its first
+ * m_u = min(B, N_u) rows: a kept row among the first m_u stays in place; each slot below m_u
+ * whose row is dropped receives a kept row from at or beyond m_u - the highest such row goes to
+ * the lowest freed slot, the next highest to the next, and so on - with its V row and its
+ * position. At most min(m_u, N_u - m_u) rows move; rows from m_u on are left as they were (stale
+ * copies). Positions are sparse after the first pass, which the score handles as any others.
+ *
+ *   K, V        device, [total_rows][d] elements of `dtype`: read and rewritten in place
+ *   pos         device int32[total_rows]: read (unless TRI_KEYS_ROTATED) and permuted with the
+ *               rows; may be NULL with TRI_KEYS_ROTATED, then no positions are kept
+ *   dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, t_now, mu  as in tri_score
+ *   B           budget per unit, >= 0
+ *   scores      device float[total_rows]: the scores, in the row order before the moves
+ *   kept_cnt    device int32[n_units]: m_u
+ *   ws, ws_bytes  workspace as in tri_select_topb, with its own size query (it also depends on B)
+ *   stream      hipStream_t or NULL
+ * Launches: score with histogram; candidates; threshold; freed-slot and mover lists; moves.
+ * No buffer may overlap another (TRI_ERR_ALIAS).
+ */
+int tri_prune_inplace(void* K, void* V, int32_t* pos, int dtype, int layout, int d, double theta,
+                      const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
+                      const int32_t* t_now, const float* mu, int B, float* scores, int32_t* kept_cnt,
+                      void* ws, size_t* ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

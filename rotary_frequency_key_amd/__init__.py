@@ -13,11 +13,15 @@ from ._abi import (  # noqa: F401
     TRI_DT_F32,
     TRI_KEYS_ROTATED,
     TRI_SELECT_HIST_FROM_SCORE,
+    InplacePlan,
     PassPlan,
     ScorePlan,
     TriError,
     library_path,
+    inplace_workspace_bytes,
+    make_inplace_workspace,
     make_workspace,
+    prune_inplace,
     prune_pass,
     prune_pass_3calls,
     workspace_bytes,

@@ -48,6 +48,9 @@ def _load():
     lib.tri_prune_pass.argtypes = [vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, vp, i32,
                                    vp, vp, vp, vp, vp, vp, vp, szp, vp]
     lib.tri_prune_pass.restype = i32
+    lib.tri_prune_inplace.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, i32,
+                                      vp, vp, vp, szp, vp]
+    lib.tri_prune_inplace.restype = i32
     return lib
 
 
@@ -310,6 +313,79 @@ def prune_pass_3calls(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=N
     K_out, V_out, pos_out = tri_compact_kv(K, V, pos, row_off, kept_idx, kept_cnt, B,
                                            K_out=K_out, V_out=V_out, pos_out=pos_out)
     return scores, kept_idx, kept_cnt, K_out, V_out, pos_out
+
+
+def inplace_workspace_bytes(n_units: int, max_rows: int, B: int) -> int:
+    """Bytes of the workspace of tri_prune_inplace."""
+    n = ctypes.c_size_t(0)
+    st = _lib.tri_prune_inplace(None, None, None, TRI_DT_BF16, TRI_BANDS_INTERLEAVED, 128, 1.0, None,
+                                int(n_units), 0, int(max_rows), None, None, int(B), None, None, None,
+                                ctypes.byref(n), None)
+    _check("tri_prune_inplace(query)", st)
+    return int(n.value)
+
+
+def make_inplace_workspace(n_units: int, max_rows: int, B: int, device) -> torch.Tensor:
+    """A tri_prune_inplace workspace in its rest state (zero-filled once, at allocation)."""
+    return torch.zeros(inplace_workspace_bytes(n_units, max_rows, B), dtype=torch.uint8, device=device)
+
+
+def _inplace_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, kept_cnt, layout):
+    _dev(K, "K", ndim=2)
+    dt = _key_dtype(K)
+    R, d = K.shape
+    _dev(V, "V", K.dtype, 2)
+    if V.shape != K.shape:
+        raise ValueError("V must have the shape of K")
+    _dev(row_off, "row_off", torch.int64, 1)
+    U = row_off.numel() - 1
+    if pos is not None or not (layout & TRI_KEYS_ROTATED):
+        _dev(pos, "pos", torch.int32, 1)
+        if pos.numel() != R:
+            raise ValueError("pos has the wrong size")
+    _dev(t_now, "t_now", torch.int32, 1)
+    _dev(mu, "mu", torch.float32)
+    if t_now.numel() != U or mu.numel() != U * d:
+        raise ValueError("t_now or mu has the wrong size")
+    if ws is None:
+        ws = make_inplace_workspace(U, max_rows, B, K.device)
+    if scores is None:
+        scores = torch.empty(R, dtype=torch.float32, device=K.device)
+    if kept_cnt is None:
+        kept_cnt = torch.empty(U, dtype=torch.int32, device=K.device)
+    _dev(ws, "ws", torch.uint8, 1)
+    _dev(scores, "scores", torch.float32, 1)
+    _dev(kept_cnt, "kept_cnt", torch.int32, 1)
+    if scores.numel() != R or kept_cnt.numel() != U:
+        raise ValueError("scores or kept_cnt has the wrong size")
+    tensors = (K, V, pos, row_off, t_now, mu, ws, scores, kept_cnt)
+    nbytes = ctypes.c_size_t(ws.numel())
+    args = (_ptr(K), _ptr(V), _ptr(pos), dt, int(layout), int(d), float(theta), _ptr(row_off), int(U), int(R),
+            int(max_rows), _ptr(t_now), _ptr(mu), int(B), _ptr(scores), _ptr(kept_cnt), _ptr(ws),
+            ctypes.byref(nbytes), _stream(K.device))
+    return tensors, nbytes, args
+
+
+def prune_inplace(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=None, scores=None, kept_cnt=None,
+                  layout=TRI_BANDS_INTERLEAVED):
+    """tri_prune_inplace: prune every unit of the cache where it lives (K, V and pos are
+    rewritten). Returns (scores, kept_cnt)."""
+    tensors, nbytes, args = _inplace_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores,
+                                          kept_cnt, layout)
+    _check("tri_prune_inplace", _lib.tri_prune_inplace(*args))
+    return tensors[7], tensors[8]
+
+
+class InplacePlan:
+    """Arguments of tri_prune_inplace marshalled once, for repeated launches."""
+
+    def __init__(self, K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws, scores, kept_cnt,
+                 layout=TRI_BANDS_INTERLEAVED):
+        self._tensors, self._nbytes, self._args = _inplace_args(
+            K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, kept_cnt, layout)
+
+    def run(self):
+        _check("tri_prune_inplace", _lib.tri_prune_inplace(*self._args))
 
 
 class ScorePlan:

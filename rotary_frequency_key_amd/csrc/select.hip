@@ -583,6 +583,114 @@ hipError_t launch_emit(const SelectArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------------------------
+// in-place pass: freed slots and the kept rows that fill them
+// ---------------------------------------------------------------------------------------------
+//
+// After the select, unit u keeps m rows. In place, the kept rows must end up in the unit's first
+// m slots. A kept row below m stays where it is; every slot below m whose row is dropped is
+// freed, and the kept rows at or beyond m fill the freed slots: the highest such row the lowest
+// free slot, the next highest the next, and so on. Only those rows move (at most
+// min(m, N_u - m)), so a steady-state pass over a cache of B + chunk rows copies at most one
+// chunk of rows instead of the B rows a full compaction would.
+//
+// mark_kernel: one wave per granule. With r's kept rank q(r) (kept rows before r):
+//   freed slot s < m   is the (s - q(s))-th freed slot
+//   kept row r >= m    is the (m - 1 - q(r))-th kept row counted from the last
+// and the wave holding row m records moves = m - q(m), the number of either.
+// move_kernel: the j-th freed slot receives the j-th kept row from the last (K, V, position);
+// sources are at or beyond m and destinations below it, so no row is both read and written.
+
+__global__ __launch_bounds__(kEN) void mark_kernel(SelectArgs a, uint32_t* hole, uint32_t* mover, uint32_t hcap) {
+  const int NG = a.lay.grans, gshift = a.lay.gran_shift;
+  const int EPU = (NG + kEW - 1) / kEW;
+  const int u = blockIdx.x / EPU, c = blockIdx.x - u * EPU;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const WsPtrs w = ws_ptrs(a);
+  const dev::UnitRows ur = dev::unit_rows(a.row_off, u, a.total_rows, a.max_rows);
+  const uint32_t n = (uint32_t)ur.n;
+  const uint32_t g = (uint32_t)(c * kEW + wave);
+  const uint32_t gc = g < (uint32_t)NG ? g : (uint32_t)NG - 1;
+  const uint32_t i0 = g << gshift;
+  const float* sc = a.scores + ur.beg;
+  UnitState* st = w.state + u;
+  const uint32_t mode = st->mode, m = st->m, T = st->T, need = st->need;
+  const uint32_t off = w.gran_off[(size_t)u * NG + gc];
+  const uint32_t E0 = w.gran_eq[(size_t)u * NG + gc];
+  const uint32_t r_first = i0 + lane;
+  const float s_first = r_first < n ? load_at(sc, r_first) : 0.f;
+  if (c == 0 && wave == 0 && lane == 0) {
+    a.kept_cnt[u] = (int32_t)m;
+    if (mode != kModeThreshold) st->moves = 0u;  // every row kept, or none: nothing moves
+  }
+  if (g >= (uint32_t)NG || i0 >= n || mode != kModeThreshold) return;  // whole wave
+  const uint32_t i1 = n - i0 > (1u << gshift) ? i0 + (1u << gshift) : n;
+  const uint32_t ties0 = E0 < need ? E0 : need;
+  uint32_t* hl = hole + (size_t)u * hcap;
+  uint32_t* ml = mover + (size_t)u * hcap;
+
+  uint32_t run_g = 0, run_e = E0;
+  for (uint32_t t0 = i0; t0 < i1; t0 += 64) {
+    const uint32_t r = t0 + lane;
+    const bool in = r < i1;
+    const uint32_t k = order_key(t0 == i0 ? s_first : load_at(sc, in ? r : i1 - 1));
+    const bool gt = in && k > T, eq = in && k == T;
+    const uint64_t mg = __ballot(gt), me = __ballot(eq);
+    const bool keep = gt || (eq && run_e + lanes_below(me) < need);
+    const uint32_t s0 = off + run_g + (run_e < need ? run_e : need) - ties0;  // kept rank of the step's first kept row
+    run_g += popc64(mg);
+    run_e += popc64(me);
+    const uint64_t mk = __ballot(keep);
+    const uint32_t q = s0 + lanes_below(mk);  // kept rows before r
+    if (in && r < m && !keep) {
+      const uint32_t j = r - q;
+      if (j < hcap) hl[j] = r;
+    }
+    if (in && r >= m && keep) {
+      const uint32_t j = m - 1 - q;
+      if (j < hcap) ml[j] = r;
+    }
+    if (t0 <= m && m - t0 < 64u && m < i1 && lane == 0) {  // the step holding row m (m < n here)
+      const uint32_t below = m - t0;  // lanes of rows before m
+      const uint64_t before = below ? (mk & (~0ull >> (64 - below))) : 0ull;
+      st->moves = m - (s0 + popc64(before));
+    }
+  }
+}
+
+template <int CPR>
+__global__ __launch_bounds__(256) void move_kernel(SelectArgs a, MoveArgs mv, int blocks_per_unit) {
+  constexpr int ROWS = 256 / CPR;
+  const int u = blockIdx.x / blocks_per_unit, b = blockIdx.x - u * blocks_per_unit;
+  const WsPtrs w = ws_ptrs(a);
+  const dev::UnitRows ur = dev::unit_rows(a.row_off, u, a.total_rows, a.max_rows);
+  const UnitState* st = w.state + u;
+  const uint32_t h = st->moves;
+  const uint32_t j = (uint32_t)(b * ROWS) + threadIdx.x / CPR;
+  const uint32_t part = threadIdx.x % CPR;
+  if (j >= h || j >= (uint32_t)mv.hcap) return;
+  const uint32_t dst = mv.hole[(size_t)u * mv.hcap + j];
+  const uint32_t src = mv.mover[(size_t)u * mv.hcap + j];
+  if (dst >= ur.n || src >= ur.n) return;  // only with an inconsistent workspace
+  const int64_t sp = (ur.beg + src) * CPR + part, dp = (ur.beg + dst) * CPR + part;
+  const uint4 kv = static_cast<const uint4*>(mv.K)[sp];
+  const uint4 vv = static_cast<const uint4*>(mv.V)[sp];
+  static_cast<uint4*>(mv.K)[dp] = kv;
+  static_cast<uint4*>(mv.V)[dp] = vv;
+  if (part == 0 && mv.pos) mv.pos[ur.beg + dst] = mv.pos[ur.beg + src];
+}
+
+template <int CPR>
+hipError_t launch_move(const SelectArgs& a, const MoveArgs& mv, hipStream_t s) {
+  constexpr int ROWS = 256 / CPR;
+  const int64_t bpu = (mv.hcap + ROWS - 1) / ROWS;
+  const int64_t grid = bpu * a.n_units;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(move_kernel<CPR>, dim3((unsigned)grid), dim3(256), 0, s, a, mv, (int)bpu);
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
@@ -607,6 +715,27 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
       case 32: e = launch_emit<32>(a, s); break;
       default: e = launch_emit<64>(a, s); break;
     }
+  }
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_select_inplace(const SelectArgs& a, const MoveArgs& mv, hipStream_t s) {
+  const int64_t U = a.n_units;
+  const int64_t cand_grid = U * a.lay.cand_wgs;
+  const int64_t mark_grid = U * ((a.lay.grans + kEW - 1) / kEW);
+  if (cand_grid > 0x7FFFFFFF || mark_grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (mv.row_bytes != 128 && mv.row_bytes != 256 && mv.row_bytes != 512 && mv.row_bytes != 1024)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(cand_kernel, dim3((unsigned)cand_grid), dim3(kCN), 0, s, a);
+  hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)U), dim3(kRN), 0, s, a);
+  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)mark_grid), dim3(kEN), 0, s, a, mv.hole, mv.mover, (uint32_t)mv.hcap);
+  hipError_t e = hipSuccess;
+  switch (mv.row_bytes / 16) {
+    case 8: e = launch_move<8>(a, mv, s); break;
+    case 16: e = launch_move<16>(a, mv, s); break;
+    case 32: e = launch_move<32>(a, mv, s); break;
+    default: e = launch_move<64>(a, mv, s); break;
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();

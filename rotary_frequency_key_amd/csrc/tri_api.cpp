@@ -309,4 +309,51 @@ int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, d
   return TRI_OK;
 }
 
+int tri_prune_inplace(void* K, void* V, int32_t* pos, int dtype, int layout, int d, double theta,
+                      const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
+                      const int32_t* t_now, const float* mu, int B, float* scores, int32_t* kept_cnt,
+                      void* ws, size_t* ws_bytes, void* stream) {
+  if (n_units < 1 || B < 0 || max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
+  const tri::InplaceLayout lay = tri::inplace_layout(n_units, max_rows, B);
+  if (ws == nullptr && ws_bytes != nullptr) {  // size query
+    *ws_bytes = lay.total;
+    return TRI_OK;
+  }
+  int st = check_score(K, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu, scores,
+                       ws, lay.total);
+  if (st != TRI_OK) return st;
+  if (max_rows > tri::kMaxSelectRows) return TRI_ERR_UNSUPPORTED;
+  if (kept_cnt == nullptr || !aligned(kept_cnt, 4)) return TRI_ERR_ARG;
+  if (!aligned(ws, 256)) return TRI_ERR_ARG;
+  const int row_bytes = d * (dtype == TRI_DT_BF16 ? 2 : 4);
+  if (total_rows > 0 && (V == nullptr || !aligned(V, 16))) return TRI_ERR_ARG;
+  // K, V and pos are read and written; none of the buffers may overlap another
+  const Range bufs[] = {span(K, total_rows * row_bytes), span(V, total_rows * row_bytes),
+                        span(pos, total_rows * 4),        span(scores, total_rows * 4),
+                        span(kept_cnt, int64_t(n_units) * 4), span(ws, static_cast<int64_t>(lay.total)),
+                        span(row_off, int64_t(n_units + 1) * 8), span(t_now, int64_t(n_units) * 4),
+                        span(mu, int64_t(n_units) * d * 4)};
+  const int nb = static_cast<int>(sizeof(bufs) / sizeof(bufs[0]));
+  for (int i = 0; i < nb; ++i)
+    for (int j = i + 1; j < nb; ++j)
+      if (overlap(bufs[i], bufs[j])) return TRI_ERR_ALIAS;
+  if (ws == nullptr || ws_bytes == nullptr || *ws_bytes < lay.total) return TRI_ERR_WORKSPACE;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_score_call(K, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu, scores,
+                        ws, s) != hipSuccess)
+    return TRI_ERR_HIP;
+  tri::SelectArgs a{};
+  a.scores = scores; a.row_off = row_off; a.n_units = n_units; a.total_rows = total_rows;
+  a.max_rows = max_rows; a.B = B; a.kept_idx = nullptr; a.kept_cnt = kept_cnt;
+  a.ws = ws;
+  a.lay = lay.sel;
+  a.hist_ready = true;
+  char* w = static_cast<char*>(ws);
+  tri::MoveArgs mv{K, V, pos, row_bytes, reinterpret_cast<uint32_t*>(w + lay.hole),
+                   reinterpret_cast<uint32_t*>(w + lay.mover), lay.hcap};
+  if (tri::launch_select_inplace(a, mv, s) != hipSuccess) return TRI_ERR_HIP;
+  return TRI_OK;
+}
+
 }  // extern "C"

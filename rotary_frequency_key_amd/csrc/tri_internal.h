@@ -44,7 +44,8 @@ struct UnitState {
   uint32_t m;       // rows kept: min(B, N_u)
   uint32_t b0;      // top digit of T
   uint32_t above0;  // keys whose top digit is above b0
-  uint32_t pad[2];
+  uint32_t moves;   // in-place pass: kept rows at or beyond slot m (= slots freed below m)
+  uint32_t pad;
 };
 constexpr uint32_t kModeThreshold = 0, kModeAll = 1, kModeNone = 2;
 
@@ -86,6 +87,27 @@ inline WsLayout ws_layout(int n_units, int64_t max_rows) {
   return L;
 }
 
+// In-place pass: the select workspace followed by the freed-slot list and the list of kept rows
+// beyond slot m, hcap entries per unit (hcap >= min(B, max_rows - B), the most rows that move).
+struct InplaceLayout {
+  WsLayout sel;
+  int64_t hcap;
+  size_t hole, mover, total;
+};
+
+inline InplaceLayout inplace_layout(int n_units, int64_t max_rows, int B) {
+  InplaceLayout L{};
+  L.sel = ws_layout(n_units, max_rows);
+  const int64_t spare = max_rows > B ? max_rows - B : 0;
+  L.hcap = spare < B ? spare : B;
+  if (L.hcap < 1) L.hcap = 1;
+  size_t off = L.sel.total;
+  L.hole = off;  off = align256(off + (size_t)n_units * L.hcap * 4);
+  L.mover = off; off = align256(off + (size_t)n_units * L.hcap * 4);
+  L.total = off;
+  return L;
+}
+
 struct ScoreArgs {
   const void* keys;
   int dtype, layout, d;  // layout: band pairing only (TRI_BANDS_*)
@@ -121,6 +143,17 @@ struct SelectArgs {
   int32_t* pos_out;
 };
 
+// In-place pass, after the threshold: freed slots below m and kept rows beyond it.
+struct MoveArgs {
+  void* K;
+  void* V;
+  int32_t* pos;  // or nullptr
+  int row_bytes;
+  uint32_t* hole;
+  uint32_t* mover;
+  int64_t hcap;
+};
+
 struct CompactArgs {
   const void* K;
   const void* V;
@@ -140,5 +173,8 @@ struct CompactArgs {
 hipError_t launch_score(const ScoreArgs& a, const BandConst& bc, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+// tri_prune_inplace after the score: threshold, then the freed slots filled with the kept rows
+// beyond them (a.K_out etc. unused).
+hipError_t launch_select_inplace(const SelectArgs& a, const MoveArgs& mv, hipStream_t s);
 
 }  // namespace tri

@@ -189,3 +189,32 @@ def test_compact_argument_errors():
     assert _compact(Vo=A["Ko"] + 256) == ALIAS
     assert _compact(po=A["kidx"]) == ALIAS
     assert _compact(Ko=A["V"] + 1024) == ALIAS
+
+
+def _inplace(**kw):
+    args = dict(K=A["keys"], V=A["V"], pos=A["pos"], dtype=1, layout=0, d=128, theta=1e6, row_off=A["row_off"],
+                U=8, R=8 * 13024, maxr=13024, t=A["t"], mu=A["mu"], B=12000, scores=A["scores"], kcnt=A["kcnt"],
+                ws=None, wsb=None)
+    args.update(kw)
+    return lib.tri_prune_inplace(args["K"], args["V"], args["pos"], args["dtype"], args["layout"], args["d"],
+                                 args["theta"], args["row_off"], args["U"], args["R"], args["maxr"], args["t"],
+                                 args["mu"], args["B"], args["scores"], args["kcnt"], args["ws"], args["wsb"], None)
+
+
+def test_prune_inplace_argument_errors():
+    n = ctypes.c_size_t(0)
+    assert _inplace(wsb=ctypes.byref(n)) == OK
+    # the select workspace of 8 x 13024 rows, then two lists of min(B, max_rows - B) = 1024 words per unit
+    m = ctypes.c_size_t(0)
+    assert _select(maxr=13024, wsb=ctypes.byref(m)) == OK
+    assert n.value == m.value + 2 * 8 * 1024 * 4
+    ok = ctypes.byref(ctypes.c_size_t(n.value))
+    assert _inplace(B=-1, ws=A["ws"], wsb=ok) == ARG
+    assert _inplace(kcnt=None, ws=A["ws"], wsb=ok) == ARG
+    assert _inplace(V=None, ws=A["ws"], wsb=ok) == ARG
+    assert _inplace(pos=None, ws=A["ws"], wsb=ok) == ARG  # positions are read unless the keys are rotated
+    assert _inplace(V=A["keys"] + 4096, ws=A["ws"], wsb=ok) == ALIAS  # V overlaps K
+    assert _inplace(kcnt=A["pos"] + 64, ws=A["ws"], wsb=ok) == ALIAS
+    assert _inplace(ws=A["ws"], wsb=ctypes.byref(ctypes.c_size_t(n.value - 1))) == WS
+    assert _inplace(ws=None, wsb=None) == WS
+    assert _inplace(maxr=(1 << 27) + 1, R=(1 << 27) + 1, U=1, ws=A["ws"], wsb=ok) == UNSUP
