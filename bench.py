@@ -291,6 +291,42 @@ def main():
             "score_kernel_gbps": alg["K"] / (rot_score_us * 1e-6) / 1e9,
         },
     }
+    # the max-over-offsets variant on the same workload: centers E[q] (not folded), 17 offsets;
+    # the pass as score_max + select + compact, and the score kernel alone (its histograms go to a
+    # workspace of their own, as for the averaged score)
+    D = np.array([1 << j for j in range(17)], dtype=np.int64)
+    centers = torch.from_numpy(np.ascontiguousarray(P["centers"], dtype=np.float32)).to(dev)
+    ws_max = tri.make_workspace(U, max_rows, dev)
+
+    def max_plan(c, ws):
+        return tri.MaxPassPlan(c["K"], c["V"], c["pos"], c["row_off"], max_rows, c["t"], centers, wl.theta, D, B,
+                               ws=ws, scores=c["scores"], kept_idx=c["kept_idx"], kept_cnt=c["kept_cnt"],
+                               K_out=c["K_out"], V_out=c["V_out"], pos_out=c["pos_out"])
+
+    mpass = [max_plan(c, c["ws"]) for c in copies]
+    mscore = [max_plan(c, ws_max) for c in copies]
+    max_times = []
+    nsteps = max(10, args.steps // 4)
+    for call in ([p.run for p in mpass], [p.score for p in mscore]):
+        for i in range(args.warmup):
+            call[i % len(call)]()
+        torch.cuda.synchronize()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
+        for i in range(nsteps):
+            call[i % len(call)]()
+        eb.record()
+        torch.cuda.synchronize()
+        max_times.append(ea.elapsed_time(eb) * 1e3 / nsteps)
+    del mpass, mscore, ws_max
+    result["max_over_offsets"] = {
+        "note": "same workload, maximum over the 17 offsets of the unfolded score; pass = three calls",
+        "us_per_pass": max_times[0],
+        "keys_per_s": R / (max_times[0] * 1e-6),
+        "score_kernel_us": max_times[1],
+        "band_offset_evals_per_s": R * (wl.d // 2) * D.size / (max_times[1] * 1e-6),
+    }
+
     # free the pass copies before the steady-state cache
     del copies, plans
     torch.cuda.empty_cache()

@@ -150,6 +150,31 @@ int tri_score(const void* keys, int dtype, int layout, int d, double theta,
               void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * tri_score_max - the maximum over the offset schedule instead of the mean.
+ *
+ *   score[r] = max_{delta in D} Re{ sum_f E[q_{u,f}] * conj(k_{r,f}) * e^{i omega_f (t_u - pos[r] + delta)} }
+ *
+ * [N] "What it saves, and what it does not": the fold needs the mean over the offsets to be
+ * linear and does not cover the variant that takes the maximum over them, so every offset is
+ * evaluated. The rotation by the offset is applied to the key's rotated product (rotations
+ * compose by adding angles, [N] "The same score, read as arrows in the plane"), so each offset
+ * costs two FMAs per band.
+ *
+ * Arguments as in tri_score, except:
+ *   offsets     host int64[n_offsets], the schedule D; 0 <= delta < 2^24 each
+ *   n_offsets   1 .. 32 (more: TRI_ERR_UNSUPPORTED)
+ *   centers     device float[n_units][F][2]: E[q_f] itself (not folded)
+ *   layout      TRI_BANDS_INTERLEAVED or TRI_BANDS_HALF_SPLIT (TRI_KEYS_ROTATED: unsupported)
+ * The workspace protocol is tri_score's: with ws, the histogram of these scores is added for
+ * tri_select_topb (TRI_SELECT_HIST_FROM_SCORE), and tri_compact_kv completes the pass.
+ * Device preconditions: 0 <= t_u - pos[r] < 2^24; finite keys and centers.
+ */
+int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, const int64_t* offsets,
+                  int n_offsets, const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
+                  const int32_t* pos, const int32_t* t_now, const float* centers, float* scores, void* ws,
+                  size_t* ws_bytes, void* stream);
+
+/*
  * tri_select_topb - keep the B highest-scoring rows of each unit.
  *
  * [N] introduction: when the cache must be trimmed, every key is scored and the

@@ -14,6 +14,7 @@ from ._abi import (  # noqa: F401
     TRI_KEYS_ROTATED,
     TRI_SELECT_HIST_FROM_SCORE,
     InplacePlan,
+    MaxPassPlan,
     PassPlan,
     ScorePlan,
     TriError,
@@ -29,5 +30,6 @@ from ._abi import (  # noqa: F401
     tri_compact_kv,
     tri_fold_weights,
     tri_score,
+    tri_score_max,
     tri_select_topb,
 )

@@ -48,6 +48,9 @@ def _load():
     lib.tri_prune_pass.argtypes = [vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, vp, i32,
                                    vp, vp, vp, vp, vp, vp, vp, szp, vp]
     lib.tri_prune_pass.restype = i32
+    lib.tri_score_max.argtypes = [vp, i32, i32, i32, ctypes.c_double, vp, i32, vp, i32, i64, i64, vp, vp, vp,
+                                  vp, vp, szp, vp]
+    lib.tri_score_max.restype = i32
     lib.tri_prune_inplace.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, i32,
                                       vp, vp, vp, szp, vp]
     lib.tri_prune_inplace.restype = i32
@@ -173,6 +176,37 @@ def tri_score(keys: torch.Tensor, row_off: torch.Tensor, max_rows: int, pos: Opt
                         int(R), int(max_rows), _ptr(pos), _ptr(t_now), _ptr(mu), _ptr(scores),
                         wsp, nbytes, _stream(keys.device))
     _check("tri_score", st)
+    return scores
+
+
+def tri_score_max(keys: torch.Tensor, row_off: torch.Tensor, max_rows: int, pos: torch.Tensor,
+                  t_now: torch.Tensor, centers: torch.Tensor, theta: float, offsets, *,
+                  layout: int = TRI_BANDS_INTERLEAVED, scores: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Maximum over the offset schedule of the unfolded score; centers are E[q] (device float32
+    [U][d/2][2]), offsets a host sequence of ints."""
+    _dev(keys, "keys", ndim=2)
+    dt = _key_dtype(keys)
+    R, d = keys.shape
+    _dev(row_off, "row_off", torch.int64, 1)
+    U = row_off.numel() - 1
+    _dev(pos, "pos", torch.int32, 1)
+    _dev(t_now, "t_now", torch.int32, 1)
+    _dev(centers, "centers", torch.float32)
+    if pos.numel() != R or t_now.numel() != U or centers.numel() != U * d:
+        raise ValueError("pos, t_now or centers has the wrong size")
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    if scores is None:
+        scores = torch.empty(R, dtype=torch.float32, device=keys.device)
+    _dev(scores, "scores", torch.float32, 1)
+    wsp, nbytes = None, None
+    if ws is not None:
+        _dev(ws, "ws", torch.uint8, 1)
+        wsp, nbytes = _ptr(ws), ctypes.byref(ctypes.c_size_t(ws.numel()))
+    st = _lib.tri_score_max(_ptr(keys), dt, int(layout), int(d), float(theta), offs.ctypes.data_as(ctypes.c_void_p),
+                            int(offs.size), _ptr(row_off), int(U), int(R), int(max_rows), _ptr(pos), _ptr(t_now),
+                            _ptr(centers), _ptr(scores), wsp, nbytes, _stream(keys.device))
+    _check("tri_score_max", st)
     return scores
 
 
@@ -386,6 +420,51 @@ class InplacePlan:
 
     def run(self):
         _check("tri_prune_inplace", _lib.tri_prune_inplace(*self._args))
+
+
+class MaxPassPlan:
+    """The max-over-offsets pass as three calls with arguments marshalled once: tri_score_max
+    (histogram into ws), tri_select_topb on that histogram, tri_compact_kv."""
+
+    def __init__(self, K, V, pos, row_off, max_rows, t_now, centers, theta, offsets, B, *, ws, scores,
+                 kept_idx, kept_cnt, K_out, V_out, pos_out, layout=TRI_BANDS_INTERLEAVED):
+        _dev(K, "K", ndim=2)
+        dt = _key_dtype(K)
+        R, d = K.shape
+        U = row_off.numel() - 1
+        for t, name in [(V, "V"), (K_out, "K_out"), (V_out, "V_out")]:
+            _dev(t, name, K.dtype)
+        for t, name in [(pos, "pos"), (t_now, "t_now"), (kept_idx, "kept_idx"), (kept_cnt, "kept_cnt"),
+                        (pos_out, "pos_out")]:
+            _dev(t, name, torch.int32)
+        _dev(row_off, "row_off", torch.int64, 1)
+        _dev(centers, "centers", torch.float32)
+        _dev(scores, "scores", torch.float32, 1)
+        _dev(ws, "ws", torch.uint8, 1)
+        if (V.shape != K.shape or pos.numel() != R or t_now.numel() != U or centers.numel() != U * d
+                or scores.numel() != R or kept_idx.numel() != U * B or kept_cnt.numel() != U
+                or K_out.numel() != U * B * d or V_out.numel() != U * B * d or pos_out.numel() != U * B):
+            raise ValueError("a tensor has the wrong size")
+        self._offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+        self._nbytes = ctypes.c_size_t(ws.numel())
+        self._tensors = (K, V, pos, row_off, t_now, centers, ws, scores, kept_idx, kept_cnt, K_out, V_out, pos_out)
+        st = _stream(K.device)
+        nb = ctypes.byref(self._nbytes)
+        self._score = (_ptr(K), dt, int(layout), int(d), float(theta), self._offs.ctypes.data_as(ctypes.c_void_p),
+                       int(self._offs.size), _ptr(row_off), int(U), int(R), int(max_rows), _ptr(pos), _ptr(t_now),
+                       _ptr(centers), _ptr(scores), _ptr(ws), nb, st)
+        self._select = (_ptr(scores), _ptr(row_off), int(U), int(R), int(max_rows), int(B), _ptr(kept_idx),
+                        _ptr(kept_cnt), _ptr(ws), nb, TRI_SELECT_HIST_FROM_SCORE, st)
+        self._compact = (_ptr(K), _ptr(V), _ptr(pos), dt, int(d), _ptr(row_off), int(U), int(R), _ptr(kept_idx),
+                         _ptr(kept_cnt), int(B), _ptr(K_out), _ptr(V_out), _ptr(pos_out), st)
+
+    def score(self):
+        _check("tri_score_max", _lib.tri_score_max(*self._score))
+
+    def run(self):
+        _check("tri_score_max", _lib.tri_score_max(*self._score))
+        _check("tri_select_topb", _lib.tri_select_topb(*self._select))
+        _check("tri_compact_kv", _lib.tri_compact_kv(*self._compact))
 
 
 class ScorePlan:

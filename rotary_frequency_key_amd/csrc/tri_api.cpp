@@ -214,6 +214,41 @@ int tri_score(const void* keys, int dtype, int layout, int d, double theta,
   return TRI_OK;
 }
 
+int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, const int64_t* offsets,
+                  int n_offsets, const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
+                  const int32_t* pos, const int32_t* t_now, const float* centers, float* scores, void* ws,
+                  size_t* ws_bytes, void* stream) {
+  if (n_units < 1) return TRI_ERR_ARG;
+  const size_t need = tri::hist_bytes(n_units);
+  if (ws == nullptr && ws_bytes != nullptr) {  // size query
+    *ws_bytes = need;
+    return TRI_OK;
+  }
+  if (offsets == nullptr || n_offsets < 1) return TRI_ERR_ARG;
+  if (n_offsets > tri::kMaxOffsets) return TRI_ERR_UNSUPPORTED;
+  tri::OffsetSet os{};
+  os.n = n_offsets;
+  for (int i = 0; i < n_offsets; ++i) {
+    if (offsets[i] < 0 || offsets[i] >= (int64_t(1) << 24)) return TRI_ERR_ARG;
+    os.delta[i] = static_cast<uint32_t>(offsets[i]);
+  }
+  if ((layout & TRI_KEYS_ROTATED) != 0) return TRI_ERR_UNSUPPORTED;
+  void* hist = nullptr;
+  if (ws_bytes != nullptr) {
+    if (*ws_bytes < need) return TRI_ERR_WORKSPACE;
+    hist = ws;
+  }
+  const int st = check_score(keys, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now,
+                             centers, scores, hist, need);
+  if (st != TRI_OK) return st;
+  tri::BandConst bc;
+  band_constants(d, theta, &bc);
+  tri::ScoreArgs a{keys, dtype, layout, d, false, row_off, n_units, total_rows, max_rows,
+                   pos, t_now, centers, scores, static_cast<uint32_t*>(hist)};
+  if (tri::launch_score_max(a, bc, os, static_cast<hipStream_t>(stream)) != hipSuccess) return TRI_ERR_HIP;
+  return TRI_OK;
+}
+
 int tri_select_topb(const float* scores, const int64_t* row_off, int n_units,
                     int64_t total_rows, int64_t max_rows, int B, int32_t* kept_idx,
                     int32_t* kept_cnt, void* ws, size_t* ws_bytes, unsigned flags,

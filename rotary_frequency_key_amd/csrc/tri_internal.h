@@ -170,7 +170,15 @@ struct CompactArgs {
   int32_t* pos_out;
 };
 
+// Offset schedule of the max-over-offsets score (each 0 <= delta < 2^24).
+constexpr int kMaxOffsets = 32;
+struct OffsetSet {
+  int n;
+  uint32_t delta[kMaxOffsets];
+};
+
 hipError_t launch_score(const ScoreArgs& a, const BandConst& bc, hipStream_t s);
+hipError_t launch_score_max(const ScoreArgs& a, const BandConst& bc, const OffsetSet& os, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 // tri_prune_inplace after the score: threshold, then the freed slots filled with the kept rows

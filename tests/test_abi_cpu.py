@@ -218,3 +218,28 @@ def test_prune_inplace_argument_errors():
     assert _inplace(ws=A["ws"], wsb=ctypes.byref(ctypes.c_size_t(n.value - 1))) == WS
     assert _inplace(ws=None, wsb=None) == WS
     assert _inplace(maxr=(1 << 27) + 1, R=(1 << 27) + 1, U=1, ws=A["ws"], wsb=ok) == UNSUP
+
+
+def _score_max(offsets=(1, 2, 4), **kw):
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    args = dict(keys=A["keys"], dtype=1, layout=0, d=128, theta=1e6, row_off=A["row_off"], U=8,
+                R=262144, maxr=32768, pos=A["pos"], t=A["t"], mu=A["mu"], scores=A["scores"],
+                ws=None, wsb=None, n=offs.size)
+    args.update(kw)
+    return lib.tri_score_max(args["keys"], args["dtype"], args["layout"], args["d"], args["theta"],
+                             offs.ctypes.data_as(ctypes.c_void_p), args["n"], args["row_off"], args["U"],
+                             args["R"], args["maxr"], args["pos"], args["t"], args["mu"], args["scores"],
+                             args["ws"], args["wsb"], None)
+
+
+def test_score_max_argument_errors():
+    n = ctypes.c_size_t(0)
+    assert _score_max(ws=None, wsb=ctypes.byref(n)) == OK and n.value == 8 * 4096 * 4
+    assert _score_max(offsets=[]) == ARG
+    assert _score_max(offsets=[1, -1]) == ARG
+    assert _score_max(offsets=[1 << 24]) == ARG
+    assert _score_max(offsets=list(range(33))) == UNSUP
+    assert _score_max(layout=0x100) == UNSUP  # rotated keys
+    assert _score_max(pos=None) == ARG
+    assert _score_max(d=96) == UNSUP
+    assert _score_max(scores=A["keys"] + 4096) == ALIAS

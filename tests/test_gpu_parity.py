@@ -253,6 +253,63 @@ def test_rotated_keys(dtype, layout):
     assert np.array_equal(alone.cpu().numpy(), out["scores"])
 
 
+@pytest.mark.parametrize("d,dtype,layout", [(128, "bf16", 0), (128, "bf16", 1), (64, "f32", 0), (256, "bf16", 0)])
+def test_max_over_offsets(d, dtype, layout):
+    """The maximum over the offsets of the unfolded score, against the oracle's literal loop; then
+    the select and the compaction on its histogram (score_max -> select -> compact)."""
+    import rotary_frequency_key_amd as tri
+
+    wl = dataclasses.replace(workload("c2"), d=d, dtype=dtype, heads=3, theta=5e5)
+    P = pack_units(wl, [0, 1, 2], [4000, 1500, 33])
+    keys = P["keys"]
+    F = d // 2
+    if layout == 1:  # the same bands stored half-split
+        perm = np.empty(d, dtype=int)
+        perm[0::2] = np.arange(F)
+        perm[1::2] = np.arange(F) + F
+        keys = np.empty_like(P["keys"])
+        keys[:, perm] = P["keys"]
+    dev = torch.device("cuda:0")
+    from tests._parity import keys_to_device, keys_to_host
+    U, B = 3, 500
+    for offsets in [O.power_of_two_offsets(), np.array([0, 3, 17, 1000, 99991], dtype=np.int64)]:
+        say(f"case max over offsets d={d} {dtype} layout={layout} |D|={offsets.size}")
+        K = keys_to_device(keys, dtype, dev)
+        V = keys_to_device(P["values"], dtype, dev)
+        pos = torch.from_numpy(P["pos"]).to(dev)
+        row_off = torch.from_numpy(P["row_off"]).to(dev)
+        t = torch.from_numpy(P["t"]).to(dev)
+        centers = torch.from_numpy(np.ascontiguousarray(P["centers"], dtype=np.float32)).to(dev)
+        ws = tri.make_workspace(U, 4000, dev)
+        scores = tri.tri_score_max(K, row_off, 4000, pos, t, centers, wl.theta, offsets, layout=layout, ws=ws)
+        kept_idx, kept_cnt = tri.tri_select_topb(scores, row_off, 4000, B, ws=ws, hist_from_score=True)
+        K_out, V_out, pos_out = tri.tri_compact_kv(K, V, pos, row_off, kept_idx, kept_cnt, B)
+        torch.cuda.synchronize()
+        s_gpu = scores.cpu().numpy()
+        kept_all, K_out = kept_idx.cpu().numpy(), keys_to_host(K_out, dtype)
+        assert ws_rest(ws)
+        omega = O.rotary_frequencies(d, wl.theta)
+        for i in range(U):
+            a, b = P["row_off"][i], P["row_off"][i + 1]
+            kb = O.as_bands(widen(P["keys"][a:b], dtype))
+            cb = O.as_bands(P["centers"][i].astype(np.float64))
+            s_ref = O.score_unfolded_max(cb, kb, O.distances(int(P["t"][i]), P["pos"][a:b]), omega, offsets)
+            scale = np.sum(np.abs(cb)[None, :] * np.abs(kb), axis=1) / F
+            err = score_error(s_gpu[a:b], s_ref, scale)
+            say(f"   unit {i}: max score error {err:.3g}")
+            assert err <= TOL, err
+            m = min(B, b - a)
+            kept = kept_all[i, :m]
+            assert np.array_equal(kept, O.select_topb(s_gpu[a:b], B))
+            from tests._parity import kept_mismatch
+            kept_mismatch(kept, s_ref, scale, B)
+            assert np.array_equal(K_out[i, :m], keys[a:b][kept])
+
+
+def ws_rest(ws):
+    return bool(np.all(ws[:3 * 4096 * 4].cpu().numpy() == 0))
+
+
 def test_half_split_layout_matches_interleaved():
     wl = workload("c2")
     P = pack_units(wl, [2, 6], [4000, 777])
