@@ -44,7 +44,7 @@ def algorithmic_bytes(wl, n_keys_total, n_units):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ["score.hip", "tri_device.h", "tri_internal.h"]:
+    for f in ["score.hip", "score_device.h", "tri_device.h", "tri_internal.h"]:
         with open(os.path.join(ROOT, "rotary_frequency_key_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
