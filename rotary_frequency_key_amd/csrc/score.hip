@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int c
   for (int m = 0; m < M; ++m) {
     const uint32_t row = min(wave_row + m * GPW, last);
     kb[m] = L::load(kbase, row, l);
-    pb[m] = ROT ? 0 : pbase[row];
+    pb[m] = ROT ? 0 : load_pos(pbase, row);
   }
 
   if constexpr (HIST) {
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int c
       for (int m = 0; m < M; ++m) {
         const uint32_t row = min(base + ROWS_ITER + m * GPW, last);
         kb[m] = L::load(kbase, row, l);
-        pb[m] = ROT ? 0 : pbase[row];
+        pb[m] = ROT ? 0 : load_pos(pbase, row);
       }
     }
     float acc[M];

