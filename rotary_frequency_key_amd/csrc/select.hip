@@ -447,6 +447,302 @@ __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// finish: resolve and emit in one kernel (units of at most kFinishMaxRows rows)
+// ---------------------------------------------------------------------------------------------
+//
+// One workgroup of 1024 threads per 64 output slots of a unit. Every workgroup of a unit
+// resolves T itself from the unit's candidates (a few thousand words, read by all of them, with
+// no communication between workgroups) and turns the per-granule counts (keys above the top
+// digit from the candidate kernel, candidates above or equal to T) into each granule's first
+// output slot. The granules whose kept rows fall into its 64 slots (at most 64 of them) are then
+// read again, one wave each, to place every kept row at its slot; the workgroup writes those
+// slots' indices and positions and gathers their K/V rows. Work per workgroup is bounded by its
+// slots, so kept rows that crowd into a few granules (high scores at nearby positions) are still
+// copied by many workgroups.
+// With more than kCandCap candidates (thousands of keys sharing T's top 12 bits), digits 2 and 3
+// and the per-granule counts come from the scores themselves, read in batches.
+
+constexpr int64_t kFinishMaxRows = int64_t(1) << 18;  // 64-row granules, at most 256 candidate workgroups
+constexpr int kFinSlots = 64;                         // output slots per workgroup
+constexpr int kFinMaxCandWgs = kFinishMaxRows >> kCandRowsShift;
+
+struct FinShared {
+  uint32_t sh[4 * kRW];
+  uint32_t found[2];
+  uint32_t nsel;
+  uint32_t cand[kCandCap];              // packed candidates: low 20 key bits << 12 | granule
+  uint32_t rhist[2][1024];              // radix bins of digits 2 and 3
+  uint32_t wgoff[kFinMaxCandWgs + 1];   // first candidate of each candidate workgroup
+  uint32_t cnt[kMaxGran];               // per granule: candidates above T (low 16 bits), equal (high 16)
+  uint32_t gsel[kFinSlots];             // granules with kept rows in this workgroup's slots,
+  uint32_t goff[kFinSlots];             //   their first kept row's slot
+  uint32_t geq[kFinSlots];              //   and the keys equal to T before them
+  uint32_t krow[kFinSlots];             // row of each of this workgroup's slots
+};
+
+// Keys of rows i0 + q*1024 + t (q < 8) of a unit of n rows; rows past n read row n - 1.
+__device__ __forceinline__ void load_key_batch(const float* s, uint32_t n, uint32_t i0, uint32_t (&k)[8]) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t r = i0 + (uint32_t)q * kRN + threadIdx.x;
+    k[q] = order_key(load_at(s, r < n ? r : n - 1));
+  }
+}
+
+// Copy of a workgroup's kept K and V rows to consecutive output rows: piece q (16 bytes) is part
+// q % CPR of output row q / CPR, whose source row (from the unit's first row) is krow[q / CPR],
+// clamped to lim. Every load of a step is issued before its stores.
+template <int CPR>
+struct PieceCopy {
+  static constexpr int kShift = CPR == 8 ? 3 : CPR == 16 ? 4 : CPR == 32 ? 5 : 6;
+  static constexpr uint32_t kRowBytes = CPR * 16;
+  const char* __restrict__ srcK;
+  const char* __restrict__ srcV;
+  char* __restrict__ dstK;
+  char* __restrict__ dstV;
+  const uint32_t* krow;  // LDS
+  uint32_t per, lim;     // pieces per tensor; last row of the unit
+
+  __device__ __forceinline__ size_t src(uint32_t q) const {
+    const uint32_t kr = krow[q >> kShift];
+    return (size_t)(kr < lim ? kr : lim) * kRowBytes + (q & (CPR - 1)) * 16u;
+  }
+  __device__ __forceinline__ uint4 ld(const char* p, size_t o) const { return *reinterpret_cast<const uint4*>(p + o); }
+  __device__ __forceinline__ void st(char* p, uint32_t q, const uint4& v) const {
+    *reinterpret_cast<uint4*>(p + q * 16u) = v;  // output row q / CPR, part q % CPR
+  }
+  // per <= 1024: one piece of K and one of V per thread
+  __device__ __forceinline__ void run1() const {
+    const uint32_t q = threadIdx.x;
+    const size_t o = src(q < per ? q : per - 1);
+    const uint4 k = ld(srcK, o), v = ld(srcV, o);
+    if (q < per) { st(dstK, q, k); st(dstV, q, v); }
+  }
+  // any count: two pieces of each per thread in flight
+  __device__ __forceinline__ void run2() const {
+    for (uint32_t q0 = 0; q0 < per; q0 += 2 * kRN) {  // uniform trip count
+      const uint32_t qa = q0 + threadIdx.x, qb = qa + kRN;
+      const size_t oa = src(qa < per ? qa : per - 1), ob = src(qb < per ? qb : per - 1);
+      const uint4 ka = ld(srcK, oa), va = ld(srcV, oa), kb = ld(srcK, ob), vb = ld(srcV, ob);
+      if (qa < per) { st(dstK, qa, ka); st(dstV, qa, va); }
+      if (qb < per) { st(dstK, qb, kb); st(dstV, qb, vb); }
+    }
+  }
+};
+
+template <int CPR>  // 16-byte pieces per K/V row; 0: no gather
+__global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
+  __shared__ FinShared L;
+  const int NG = a.lay.grans;
+  const int u = blockIdx.x / wpu, c = blockIdx.x - u * wpu;
+  const uint32_t t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const WsPtrs w = ws_ptrs(a);
+  const dev::UnitRows ur = dev::unit_rows(a.row_off, u, a.total_rows, a.max_rows);
+  const uint32_t n = (uint32_t)ur.n;
+  const uint32_t m = (uint32_t)a.B < n ? (uint32_t)a.B : n;
+  int32_t* out = a.kept_idx + (int64_t)u * a.B;
+  if (c == 0) {  // the unit's histogram back to rest (the candidate kernel has read it), padding, count
+    static_assert(kHistBins == 4 * kRN, "one uint4 of bins per thread");
+    reinterpret_cast<uint4*>(w.hist + (size_t)u * kHistBins)[t] = make_uint4(0u, 0u, 0u, 0u);
+    for (uint32_t j = m + t; j < (uint32_t)a.B; j += kRN) out[j] = -1;
+    if (t == 0) a.kept_cnt[u] = (int32_t)m;
+  }
+  const uint32_t s0 = (uint32_t)c * kFinSlots;
+  if (s0 >= m) return;
+  const uint32_t ns = m - s0 < (uint32_t)kFinSlots ? m - s0 : (uint32_t)kFinSlots;  // this workgroup's slots
+  const float* s = a.scores + ur.beg;
+
+  if (m == n) {  // every row kept: slot = row
+    if (t < ns) L.krow[t] = s0 + t;
+    __syncthreads();
+  } else {
+    const UnitState* st = w.state + u;
+    const uint32_t b0 = st->b0, above0 = st->above0;
+    const uint32_t nwg = ((n - 1) >> kCandRowsShift) + 1;  // candidate workgroups of this unit (<= 256)
+    const uint32_t ngu = ((n - 1) >> kGranMinShift) + 1;   // granules of this unit (<= 4096)
+    const uint32_t* cin = w.cand + (((size_t)u * a.lay.cand_wgs) << kCandRowsShift);
+    // loads: candidate counts, per-granule counts above the top digit, and a share of the
+    // candidates of workgroup cw = t / tpw (entries ci + k*tpw, inside the region whatever the count)
+    uint32_t lg = 0;
+    while ((1u << lg) < nwg) ++lg;
+    const uint32_t tpw = (kRN >> lg) < kRN / 8 ? (kRN >> lg) : kRN / 8;  // threads per workgroup (>= 4)
+    const uint32_t cw = t / tpw, ci = t % tpw;
+    const bool pre_ok = cw < nwg;
+    uint32_t pv[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) pv[k] = pre_ok ? cin[((size_t)cw << kCandRowsShift) + ci + k * tpw] : 0u;
+    const uint32_t wc = t < nwg ? w.wg_cnt[(size_t)u * a.lay.cand_wgs + t] : 0u;
+    uint32_t ggt[kRPer];
+#pragma unroll
+    for (int q = 0; q < kRPer; ++q) {
+      const uint32_t i = kRPer * t + q;
+      ggt[q] = i < ngu ? w.gran_gt[(size_t)u * NG + i] : 0u;
+      L.cnt[i] = 0u;
+    }
+    L.rhist[0][t] = 0u;
+    L.rhist[1][t] = 0u;
+    if (t == 0) L.nsel = 0u;
+    uint32_t nc;
+    const uint32_t wex = dev::block_excl_scan_dpp<kRN>(wc, L.sh, &nc);
+    if (t < nwg) L.wgoff[t] = wex;
+    if (t == 0) L.wgoff[nwg] = nc;
+    __syncthreads();
+
+    uint32_t r = m - above0, above, T, need;
+    if (nc <= (uint32_t)kCandCap) {
+      // ---- place the candidates, counting digit 2
+      if (pre_ok) {
+        const uint32_t base = L.wgoff[cw], cnt_w = L.wgoff[cw + 1] - base;
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+          const uint32_t i = ci + k * tpw;
+          if (i < cnt_w) {
+            L.cand[base + i] = pv[k];
+            atomicAdd(&L.rhist[0][cand_d2(pv[k])], 1u);
+          }
+        }
+        for (uint32_t i = tpw * kPre + ci; i < cnt_w; i += tpw) {
+          const uint32_t v = cin[((size_t)cw << kCandRowsShift) + i];
+          L.cand[base + i] = v;
+          atomicAdd(&L.rhist[0][cand_d2(v)], 1u);
+        }
+      }
+      __syncthreads();
+      const uint32_t v2[1] = {L.rhist[0][1023 - t]};
+      const uint32_t d2 = block_find<kRN, 1>(v2, 1024, r, L.sh, L.found, &above);
+      r -= above;
+      for (uint32_t j = t; j < nc; j += kRN) {
+        const uint32_t p = L.cand[j];
+        if (cand_d2(p) == d2) atomicAdd(&L.rhist[1][cand_d3(p)], 1u);
+      }
+      __syncthreads();
+      const uint32_t v3[1] = {L.rhist[1][1023 - t]};
+      const uint32_t d3 = block_find<kRN, 1>(v3, 1024, r, L.sh, L.found, &above);
+      T = (((b0 << 10) | d2) << 10) | d3;
+      need = r - above;
+      // candidates above T and equal to it, per granule
+      const uint32_t lowT = T & 0xFFFFFu;
+      for (uint32_t j = t; j < nc; j += kRN) {
+        const uint32_t p = L.cand[j], lk = p >> 12;
+        if (lk >= lowT) atomicAdd(&L.cnt[p & 0xFFFu], lk > lowT ? 1u : 0x10000u);
+      }
+    } else {
+      // ---- more candidates than LDS holds: from the scores
+      uint32_t pre = b0;
+#pragma unroll 1
+      for (int digit = 0; digit < 2; ++digit) {
+        const int sh = digit == 0 ? 10 : 0;
+        uint32_t* rh = L.rhist[digit];
+        for (uint32_t i0 = 0; i0 < n; i0 += 8 * kRN) {
+          uint32_t kk[8];
+          load_key_batch(s, n, i0, kk);
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (i0 + (uint32_t)q * kRN + t < n && (kk[q] >> (sh + 10)) == pre) atomicAdd(&rh[(kk[q] >> sh) & 1023u], 1u);
+        }
+        __syncthreads();
+        const uint32_t v[1] = {rh[1023 - t]};
+        const uint32_t b = block_find<kRN, 1>(v, 1024, r, L.sh, L.found, &above);
+        r -= above;
+        pre = (pre << 10) | b;
+      }
+      T = pre;
+      need = r;
+      for (uint32_t i0 = 0; i0 < n; i0 += 8 * kRN) {
+        uint32_t kk[8];
+        load_key_batch(s, n, i0, kk);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t i = i0 + (uint32_t)q * kRN + t;
+          if (i < n && (kk[q] >> kHistShift) == b0 && kk[q] >= T)
+            atomicAdd(&L.cnt[i >> kGranMinShift], kk[q] > T ? 1u : 0x10000u);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- each granule's first slot; list the granules with kept rows in [s0, s0 + ns)
+    uint32_t kgt[kRPer], keq[kRPer], sg = 0, se = 0;
+#pragma unroll
+    for (int q = 0; q < kRPer; ++q) {
+      const uint32_t cc = L.cnt[kRPer * t + q];
+      kgt[q] = ggt[q] + (cc & 0xFFFFu);
+      keq[q] = cc >> 16;
+      sg += kgt[q];
+      se += keq[q];
+    }
+    uint32_t G, E, tg, te;
+    dev::block_excl_scan2_dpp<kRN>(sg, se, L.sh, &G, &E, &tg, &te);
+#pragma unroll
+    for (int q = 0; q < kRPer; ++q) {
+      const uint32_t first = G + (E < need ? E : need);
+      const uint32_t E1 = E + keq[q];
+      const uint32_t end = G + kgt[q] + (E1 < need ? E1 : need);
+      if (end > first && first < s0 + ns && end > s0) {
+        const uint32_t i = atomicAdd(&L.nsel, 1u);
+        if (i < (uint32_t)kFinSlots) {  // always, with a consistent workspace
+          L.gsel[i] = kRPer * t + q;
+          L.goff[i] = first;
+          L.geq[i] = E;
+        }
+      }
+      G += kgt[q];
+      E = E1;
+    }
+    __syncthreads();
+
+    // ---- the listed granules' rows, one wave per granule: every kept row to its slot
+    const uint32_t nsel = L.nsel < (uint32_t)kFinSlots ? L.nsel : (uint32_t)kFinSlots;
+    constexpr int kGW = kFinSlots / kRW;  // granules per wave, at most
+    uint32_t kk[kGW];
+#pragma unroll
+    for (int i = 0; i < kGW; ++i) {
+      const uint32_t j = (uint32_t)(i * kRW + wave);
+      const uint32_t row = j < nsel ? (L.gsel[j] << kGranMinShift) + lane : 0u;
+      kk[i] = order_key(load_at(s, row < n ? row : n - 1));
+    }
+#pragma unroll
+    for (int i = 0; i < kGW; ++i) {
+      const uint32_t j = (uint32_t)(i * kRW + wave);
+      if (j >= nsel) break;  // uniform
+      const uint32_t row = (L.gsel[j] << kGranMinShift) + lane;
+      const bool in = row < n;
+      const bool gt = in && kk[i] > T, eq = in && kk[i] == T;
+      const bool keep = gt || (eq && L.geq[j] + lanes_below(__ballot(eq)) < need);
+      const uint32_t slot = L.goff[j] + lanes_below(__ballot(keep));
+      if (keep && slot >= s0 && slot < s0 + ns) L.krow[slot - s0] = row;
+    }
+    __syncthreads();
+  }
+
+  // ---- this workgroup's slots: indices, positions, K/V rows
+  const uint32_t my_row = t < ns ? (L.krow[t] < n ? L.krow[t] : n - 1) : 0u;
+  const int64_t obase = (int64_t)u * a.B + s0;
+  if constexpr (CPR > 0) {
+    constexpr int64_t RB = CPR * 16;
+    const int32_t pos_v = a.pos_out ? a.pos[ur.beg + my_row] : 0;  // in range for every thread
+    const PieceCopy<CPR> cp{static_cast<const char*>(a.K) + ur.beg * RB, static_cast<const char*>(a.V) + ur.beg * RB,
+                            static_cast<char*>(a.K_out) + obase * RB, static_cast<char*>(a.V_out) + obase * RB,
+                            L.krow, ns * CPR, n - 1};
+    if (cp.per <= (uint32_t)kRN) cp.run1();
+    else cp.run2();
+    if (a.pos_out && t < ns) a.pos_out[obase + t] = pos_v;
+  }
+  if (t < ns) out[s0 + t] = (int32_t)my_row;
+}
+
+template <int CPR>
+hipError_t launch_finish(const SelectArgs& a, hipStream_t s) {
+  const int64_t mm = a.B < a.max_rows ? a.B : a.max_rows;
+  const int64_t wpu = mm > 0 ? (mm + kFinSlots - 1) / kFinSlots : 1;
+  const int64_t grid = (int64_t)a.n_units * wpu;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(finish_kernel<CPR>, dim3((unsigned)grid), dim3(kRN), 0, s, a, (int)wpu);
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------------------------
 // emit (and gather)
 // ---------------------------------------------------------------------------------------------
 
@@ -691,6 +987,153 @@ hipError_t launch_move(const SelectArgs& a, const MoveArgs& mv, hipStream_t s) {
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------------------------
+// units of at most 64k rows: the whole select in one workgroup per unit
+// ---------------------------------------------------------------------------------------------
+//
+// topb_kernel holds a unit's order keys in registers (KPT per thread; element j of thread t is
+// row j*1024 + t, so element j of wave w is the 64-row granule 16j + w) and runs the three radix
+// digits there: bits 31..20 from the histogram, 19..10 and 9..0 by LDS histograms over the keys
+// that share the digits found so far. Per-granule counts of keys above and equal to T, one
+// block scan of both, and every kept row's output slot follows: kept rows before its granule plus
+// kept lanes below it. It writes the kept indices (or, for the in-place pass, the freed-slot and
+// mover lists and the move count) itself, so the pass needs no candidate, resolve or emit kernel;
+// the K/V rows are then gathered by the compaction kernel.
+
+constexpr int kTN = 1024;
+constexpr int kTW = kTN / 64;
+constexpr int64_t kTopbMaxRows = 64 * kTN;
+
+struct TopbShared {
+  uint32_t sh[4 * kTW];
+  uint32_t found[2];
+  uint32_t rhist[2][1024];  // radix bins of digits 2 and 3
+  uint32_t gt[kTN];         // per granule: keys above T, then kept rows before the granule
+  uint32_t eq[kTN];         // per granule: keys equal to T, then those before the granule
+};
+
+struct InplaceOut {
+  uint32_t* hole;
+  uint32_t* mover;
+  uint32_t hcap;
+};
+
+template <int KPT, bool INPLACE>
+__global__ __launch_bounds__(kTN) void topb_kernel(SelectArgs a, InplaceOut io) {
+  static_assert(KPT * kTN <= kTopbMaxRows && KPT * (kTN / 64) <= kTN, "one granule per thread");
+  __shared__ TopbShared L;
+  const int u = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const WsPtrs w = ws_ptrs(a);
+  const dev::UnitRows ur = dev::unit_rows(a.row_off, u, a.total_rows, a.max_rows);
+  const uint32_t n = (uint32_t)ur.n;
+  const uint32_t m = (uint32_t)a.B < n ? (uint32_t)a.B : n;
+  uint4* hist4 = reinterpret_cast<uint4*>(w.hist + (size_t)u * kHistBins);
+  int32_t* out = a.kept_idx ? a.kept_idx + (int64_t)u * a.B : nullptr;
+  static_assert(kHistBins == 4 * kTN, "one uint4 of bins per thread");
+
+  if (m == n || m == 0) {  // every row kept, or none: no threshold
+    hist4[t] = make_uint4(0u, 0u, 0u, 0u);
+    if (out)
+      for (uint32_t j = t; j < (uint32_t)a.B; j += kTN) out[j] = j < m ? (int32_t)j : -1;
+    if (t == 0) {
+      a.kept_cnt[u] = (int32_t)m;
+      if constexpr (INPLACE) w.state[u].moves = 0u;
+    }
+    return;
+  }
+
+  // loads: 4 histogram bins (4095-4t down to 4092-4t) and the keys
+  const uint4 h = hist4[kTN - 1 - t];
+  const float* s = a.scores + ur.beg;
+  uint32_t k[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {  // unconditional (rows past the unit read its last row): all in flight
+    const uint32_t row = (uint32_t)j * kTN + t;
+    k[j] = order_key(load_at(s, row < n ? row : n - 1));
+  }
+  L.rhist[0][t] = 0u;
+  L.rhist[1][t] = 0u;
+
+  // digit 1 from the histogram, then the histogram back to rest
+  uint32_t above;
+  const uint32_t hv[4] = {h.w, h.z, h.y, h.x};
+  const uint32_t b0 = block_find<kTN, 4>(hv, kHistBins, m, L.sh, L.found, &above);
+  hist4[kTN - 1 - t] = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t r = m - above;
+  // digit 2 among the keys with T's digit 1
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if ((uint32_t)j * kTN + t < n && (k[j] >> 20) == b0) atomicAdd(&L.rhist[0][(k[j] >> 10) & 1023u], 1u);
+  __syncthreads();
+  const uint32_t v2[1] = {L.rhist[0][1023 - t]};
+  const uint32_t p2 = (b0 << 10) | block_find<kTN, 1>(v2, 1024, r, L.sh, L.found, &above);
+  r -= above;
+  // digit 3 among the keys with T's digits 1 and 2
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if ((uint32_t)j * kTN + t < n && (k[j] >> 10) == p2) atomicAdd(&L.rhist[1][k[j] & 1023u], 1u);
+  __syncthreads();
+  const uint32_t v3[1] = {L.rhist[1][1023 - t]};
+  const uint32_t T = (p2 << 10) | block_find<kTN, 1>(v3, 1024, r, L.sh, L.found, &above);
+  const uint32_t need = r - above;  // keys equal to T that are kept, lowest rows first
+
+  // per granule: keys above T and equal to it
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if ((uint32_t)j * kTN >= n) break;  // uniform
+    const bool in = (uint32_t)j * kTN + t < n;
+    const uint64_t mg = __ballot(in && k[j] > T), me = __ballot(in && k[j] == T);
+    if (lane == 0) {
+      L.gt[j * kTW + wave] = popc64(mg);
+      L.eq[j * kTW + wave] = popc64(me);
+    }
+  }
+  __syncthreads();
+  const uint32_t ngr = (n + 63) >> 6;
+  uint32_t G, E, tg, te;
+  dev::block_excl_scan2_dpp<kTN>((uint32_t)t < ngr ? L.gt[t] : 0u, (uint32_t)t < ngr ? L.eq[t] : 0u, L.sh, &G, &E,
+                                 &tg, &te);
+  if ((uint32_t)t < ngr) {
+    L.gt[t] = G + (E < need ? E : need);  // kept rows before granule t
+    L.eq[t] = E;                          // keys equal to T before granule t
+  }
+  __syncthreads();
+
+  // every kept row's slot: kept rows before its granule plus kept lanes below it
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if ((uint32_t)j * kTN >= n) break;  // uniform
+    const uint32_t row = (uint32_t)j * kTN + t;
+    const bool in = row < n;
+    const bool gt = in && k[j] > T, eq = in && k[j] == T;
+    const uint32_t g = (uint32_t)(j * kTW + wave);
+    const uint32_t e0 = L.eq[g], off = L.gt[g];
+    const bool keep = gt || (eq && e0 + lanes_below(__ballot(eq)) < need);
+    const uint32_t q = off + lanes_below(__ballot(keep));  // kept rows before this row
+    if (out && keep) out[q] = (int32_t)row;
+    if constexpr (INPLACE) {
+      if (in && row < m && !keep && row - q < io.hcap) io.hole[(size_t)u * io.hcap + row - q] = row;
+      if (in && row >= m && keep && m - 1 - q < io.hcap) io.mover[(size_t)u * io.hcap + m - 1 - q] = row;
+      if (row == m) w.state[u].moves = m - q;  // m < n here
+    }
+  }
+  if (out)
+    for (uint32_t j = m + t; j < (uint32_t)a.B; j += kTN) out[j] = -1;
+  if (t == 0) a.kept_cnt[u] = (int32_t)m;
+}
+
+template <bool INPLACE>
+hipError_t launch_topb(const SelectArgs& a, const InplaceOut& io, hipStream_t s) {
+  const dim3 g((unsigned)a.n_units), b(kTN);
+  if (a.max_rows <= 4 * kTN) hipLaunchKernelGGL((topb_kernel<4, INPLACE>), g, b, 0, s, a, io);
+  else if (a.max_rows <= 8 * kTN) hipLaunchKernelGGL((topb_kernel<8, INPLACE>), g, b, 0, s, a, io);
+  else if (a.max_rows <= 16 * kTN) hipLaunchKernelGGL((topb_kernel<16, INPLACE>), g, b, 0, s, a, io);
+  else if (a.max_rows <= 32 * kTN) hipLaunchKernelGGL((topb_kernel<32, INPLACE>), g, b, 0, s, a, io);
+  else hipLaunchKernelGGL((topb_kernel<64, INPLACE>), g, b, 0, s, a, io);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
@@ -704,6 +1147,18 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (!a.hist_ready && hpu > 0)
     hipLaunchKernelGGL(hist_kernel, dim3((unsigned)(U * hpu)), dim3(kHN), 0, s, a, (int)hpu);
   hipLaunchKernelGGL(cand_kernel, dim3((unsigned)cand_grid), dim3(kCN), 0, s, a);
+  if (a.max_rows <= kFinishMaxRows) {
+    hipError_t e = hipSuccess;
+    switch (a.K_out == nullptr ? 0 : a.row_bytes / 16) {
+      case 0: e = launch_finish<0>(a, s); break;
+      case 8: e = launch_finish<8>(a, s); break;
+      case 16: e = launch_finish<16>(a, s); break;
+      case 32: e = launch_finish<32>(a, s); break;
+      default: e = launch_finish<64>(a, s); break;
+    }
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)U), dim3(kRN), 0, s, a);
   hipError_t e = hipSuccess;
   if (a.K_out == nullptr) {
@@ -727,10 +1182,15 @@ hipError_t launch_select_inplace(const SelectArgs& a, const MoveArgs& mv, hipStr
   if (cand_grid > 0x7FFFFFFF || mark_grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (mv.row_bytes != 128 && mv.row_bytes != 256 && mv.row_bytes != 512 && mv.row_bytes != 1024)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(cand_kernel, dim3((unsigned)cand_grid), dim3(kCN), 0, s, a);
-  hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)U), dim3(kRN), 0, s, a);
-  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)mark_grid), dim3(kEN), 0, s, a, mv.hole, mv.mover, (uint32_t)mv.hcap);
   hipError_t e = hipSuccess;
+  if (a.max_rows <= kTopbMaxRows) {
+    e = launch_topb<true>(a, InplaceOut{mv.hole, mv.mover, (uint32_t)mv.hcap}, s);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL(cand_kernel, dim3((unsigned)cand_grid), dim3(kCN), 0, s, a);
+    hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)U), dim3(kRN), 0, s, a);
+    hipLaunchKernelGGL(mark_kernel, dim3((unsigned)mark_grid), dim3(kEN), 0, s, a, mv.hole, mv.mover, (uint32_t)mv.hcap);
+  }
   switch (mv.row_bytes / 16) {
     case 8: e = launch_move<8>(a, mv, s); break;
     case 16: e = launch_move<16>(a, mv, s); break;

@@ -14,6 +14,11 @@ import oracle as O
 
 TOL = 2e-3
 
+# The library selects in one workgroup per unit when max_rows <= 65536 (keys held in registers)
+# and with the candidate / resolve / emit kernels above that. max_rows is only an upper bound on
+# the unit lengths, so passing this value runs the second path on short units.
+SPLIT_ROWS = 65537
+
 
 def gen_workers():
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()

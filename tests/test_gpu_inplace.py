@@ -15,7 +15,7 @@ import torch
 
 import oracle as O
 from synthgen import unit_inputs, workload
-from tests._parity import TOL, keys_to_device, keys_to_host, kept_mismatch, score_error, widen
+from tests._parity import SPLIT_ROWS, TOL, keys_to_device, keys_to_host, kept_mismatch, score_error, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -61,14 +61,15 @@ class Cache:
         _, mu = tri.tri_fold_weights(wl.d, wl.theta, O.power_of_two_offsets(), centers)
         self.mu = mu
 
-    def run(self, B):
+    def run(self, B, max_rows=None):
         import rotary_frequency_key_amd as tri
 
         d = self.dev
         K = keys_to_device(self.K, self.wl.dtype, d)
         V = keys_to_device(self.V, self.wl.dtype, d)
         pos = torch.from_numpy(self.pos).to(d)
-        max_rows = int(self.lengths.max()) if self.lengths.size else 0
+        if max_rows is None:
+            max_rows = int(self.lengths.max()) if self.lengths.size else 0
         scores, kept_cnt = tri.prune_inplace(K, V, pos, torch.from_numpy(self.row_off).to(d), max_rows,
                                              torch.from_numpy(self.t).to(d), torch.from_numpy(self.mu).to(d),
                                              self.wl.theta, B)
@@ -76,9 +77,9 @@ class Cache:
         return (scores.cpu().numpy(), kept_cnt.cpu().numpy(), keys_to_host(K, self.wl.dtype),
                 keys_to_host(V, self.wl.dtype), pos.cpu().numpy())
 
-    def check_pass(self, B, label):
+    def check_pass(self, B, label, max_rows=None):
         """Run one in-place pass and check it; then adopt the expected arrangement."""
-        scores, kept_cnt, K, V, pos = self.run(B)
+        scores, kept_cnt, K, V, pos = self.run(B, max_rows)
         worst = 0.0
         for u in range(len(self.lengths)):
             a, b = self.row_off[u], self.row_off[u + 1]
@@ -104,7 +105,8 @@ class Cache:
         return worst
 
 
-def test_inplace_single_pass_edges():
+@pytest.mark.parametrize("max_rows", [None, SPLIT_ROWS])
+def test_inplace_single_pass_edges(max_rows):
     """Ragged units in one call: empty, shorter than B, equal to B, and longer; budgets 0, 1 and
     more."""
     wl = dataclasses.replace(workload("c2"), heads=6)
@@ -115,13 +117,13 @@ def test_inplace_single_pass_edges():
     pos = np.concatenate([p["pos"] for p in parts]).astype(np.int32)
     centers = np.stack([p["center"] for p in parts])
     for B in [0, 1, 300, 2500]:
-        say(f"case in-place single pass B={B}")
+        say(f"case in-place single pass B={B} max_rows={max_rows}")
         c = Cache(wl, K, V, pos, lengths, [max(n, 1) for n in lengths], centers)
-        c.check_pass(B, f"single B={B}")
+        c.check_pass(B, f"single B={B}", max_rows)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_inplace_steady_state(dtype):
+@pytest.mark.parametrize("dtype,max_rows", [("bf16", None), ("f32", None), ("bf16", SPLIT_ROWS)])
+def test_inplace_steady_state(dtype, max_rows):
     """Pass 0 prunes 20000 rows per unit to B = 3000; then three times a 1024-row chunk with the
     next positions is appended and the 4024 rows are pruned back to 3000."""
     wl = dataclasses.replace(workload("c5"), dtype=dtype, seqs=1, layers=1, heads=4)
@@ -134,7 +136,7 @@ def test_inplace_steady_state(dtype):
     V = np.concatenate([p["values"][:N0] for p in parts])
     pos = np.concatenate([p["pos"][:N0] for p in parts]).astype(np.int32)
     c = Cache(wl, K, V, pos, [N0] * U, [N0] * U, centers)
-    c.check_pass(B, "pass 0")
+    c.check_pass(B, "pass 0", max_rows)
     for k in range(1, passes + 1):
         lo, hi = N0 + (k - 1) * chunk, N0 + k * chunk
         Kn, Vn, Pn = [], [], []
@@ -146,7 +148,7 @@ def test_inplace_steady_state(dtype):
         t = hi
         c = Cache(wl, np.concatenate(Kn), np.concatenate(Vn), np.concatenate(Pn), [B + chunk] * U, [t] * U, centers)
         say(f"case in-place steady state {dtype}: pass {k} (positions sparse: {np.unique(np.diff(np.sort(c.pos[:B]))).size} gaps)")
-        err = c.check_pass(B, f"pass {k}")
+        err = c.check_pass(B, f"pass {k}", max_rows)
         say(f"   worst score error {err:.3g}")
 
 

@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 from synthgen import pack_units, workload
-from tests._parity import TOL, candidate_profile, check_unit, gen_workers, oracle_unit, run_gpu, score_error, widen
+from tests._parity import SPLIT_ROWS, TOL, candidate_profile, check_unit, gen_workers, oracle_unit, run_gpu, score_error, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -42,12 +42,13 @@ def test_c2_full():
         worst, total = max(worst, err), total + mism
     say(f"c2 worst score err {worst:.3g}, kept mismatches in band {total}")
     assert out["ws_after"]
-    # the three separate calls, and the standalone select (its own histogram), give the same bits
-    for path in ["calls", "standalone"]:
-        out2 = run_gpu(P, wl, wl.budget, path=path)
+    # the three separate calls, the standalone select (its own histogram) and the split select
+    # path (candidate, resolve, emit kernels) give the same bits
+    for path, mr in [("calls", None), ("standalone", None), ("fused", SPLIT_ROWS), ("standalone", SPLIT_ROWS)]:
+        out2 = run_gpu(P, wl, wl.budget, path=path, max_rows=mr)
         for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
-            assert np.array_equal(out2[k], out[k]), (path, k)
-        assert out2["ws_after"], path
+            assert np.array_equal(out2[k], out[k]), (path, mr, k)
+        assert out2["ws_after"], (path, mr)
     # deterministic: a second pass is bitwise identical
     out3 = run_gpu(P, wl, wl.budget)
     for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
@@ -81,7 +82,8 @@ def test_c3_full_size_sampled():
     say(f"c3 worst sampled score err {worst:.3g}")
 
 
-def test_edge_cases_ragged_units():
+@pytest.mark.parametrize("max_rows", [None, SPLIT_ROWS])
+def test_edge_cases_ragged_units(max_rows):
     """Empty, one-row, tail-sized and multi-chunk units in one launch; budgets 0, 1, between,
     equal to and above the unit sizes."""
     wl = workload("c2")
@@ -89,8 +91,8 @@ def test_edge_cases_ragged_units():
     units = list(range(len(lengths)))
     P = pack_units(dataclasses.replace(wl, heads=len(lengths)), units, lengths)
     for B in [0, 1, 300, 2048, 5000]:
-        say(f"case edge ragged B={B}")
-        out = run_gpu(P, wl, B)
+        say(f"case edge ragged B={B} max_rows={max_rows}")
+        out = run_gpu(P, wl, B, max_rows=max_rows)
         for i in range(len(lengths)):
             check_unit(P, i, wl, out, B, label=f"edge B={B}")
         assert out["ws_after"]
@@ -122,14 +124,16 @@ def test_zero_center_all_ties():
     check_unit(P, 1, wl, out, 1000, s_ref=s_ref, scale=scale, label="zero-center")
 
 
-def test_zero_center_large_tie_group():
-    """40000 tied keys: more candidates than the candidate buffer holds (the fallback path)."""
+@pytest.mark.parametrize("long_len", [65536, 70000])
+def test_zero_center_large_tie_group(long_len):
+    """40000 tied keys: more candidates than the candidate buffer holds (the fallback path of the
+    split select); with units up to 65536 rows, the one-workgroup select on all-tied keys."""
     wl = workload("c2")
-    P = pack_units(wl, [0, 1, 2], [40000, 9000, 70000])
+    P = pack_units(wl, [0, 1, 2], [40000, 9000, long_len])
     centers = P["centers"].copy()
     centers[0] = 0.0
     centers[2] = 0.0
-    say("case zero center, 40000 and 70000 ties")
+    say(f"case zero center, 40000 and {long_len} ties")
     for path in ["fused", "calls"]:
         out = run_gpu(P, wl, 2048, centers=centers, path=path)
         assert np.array_equal(out["kept_idx"][0], np.arange(2048))
@@ -139,7 +143,8 @@ def test_zero_center_large_tie_group():
         assert out["ws_after"]
 
 
-def test_quantized_scores_heavy_ties():
+@pytest.mark.parametrize("max_rows", [None, SPLIT_ROWS])
+def test_quantized_scores_heavy_ties(max_rows):
     """Keys drawn from few values so that many scores tie exactly; kept rows must follow the
     lower-index rule across chunk boundaries."""
     wl = dataclasses.replace(workload("c2"), heads=2)
@@ -148,14 +153,15 @@ def test_quantized_scores_heavy_ties():
     from synthgen import f32_to_bf16_bits
     P["keys"] = f32_to_bf16_bits(rng.choice([-1.0, 0.5, 2.0], size=P["keys"].shape).astype(np.float32))
     P["pos"] = np.zeros_like(P["pos"])  # one distance: scores depend on the key only
-    say("case quantized keys")
+    say(f"case quantized keys max_rows={max_rows}")
     for path in ["fused", "calls"]:
-        out = run_gpu(P, wl, 3000, path=path)
+        out = run_gpu(P, wl, 3000, path=path, max_rows=max_rows)
         for i in range(2):
             check_unit(P, i, wl, out, 3000, label=f"quantized {path}")
 
 
-def test_dense_candidate_workgroup():
+@pytest.mark.parametrize("max_rows", [None, SPLIT_ROWS])
+def test_dense_candidate_workgroup(max_rows):
     """1100 rows of one unit share one key and one position, so their scores tie exactly, and the
     budget puts the threshold inside that group: one candidate workgroup holds many more
     candidates than the resolve kernel preloads per workgroup, and the tie group is longer than
@@ -166,10 +172,10 @@ def test_dense_candidate_workgroup():
     P["pos"][5000:6100] = P["pos"][5000]
     s_ref, scale = oracle_unit(P, 0, wl)
     above = int(np.sum(s_ref > s_ref[5000]))
-    say(f"case dense candidate workgroup ({above} rows above the tie group)")
+    say(f"case dense candidate workgroup ({above} rows above the tie group) max_rows={max_rows}")
     for extra in [1, 550, 1100]:
         B = above + extra
-        out = run_gpu(P, wl, B)
+        out = run_gpu(P, wl, B, max_rows=max_rows)
         check_unit(P, 0, wl, out, B, s_ref=s_ref, scale=scale, label=f"dense-cand +{extra}")
         nc, per_group, tie22 = candidate_profile(out["scores"], B)
         if extra < 1100:  # the threshold is the tie group's score
