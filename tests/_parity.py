@@ -14,10 +14,12 @@ import oracle as O
 
 TOL = 2e-3
 
-# The library selects in one workgroup per unit when max_rows <= 65536 (keys held in registers)
-# and with the candidate / resolve / emit kernels above that. max_rows is only an upper bound on
-# the unit lengths, so passing this value runs the second path on short units.
-SPLIT_ROWS = 65537
+# The library picks its select kernels from max_rows: units of up to 2^18 rows take the fused
+# resolve-and-emit kernel (the in-place pass, up to 2^16 rows: one workgroup per unit with the
+# keys in registers); longer units take the candidate / resolve / emit (or mark) kernels. max_rows
+# is only an upper bound on the unit lengths, so passing this value runs the second path on
+# short units.
+SPLIT_ROWS = (1 << 18) + 1
 
 
 def gen_workers():

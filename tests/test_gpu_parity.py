@@ -124,18 +124,18 @@ def test_zero_center_all_ties():
     check_unit(P, 1, wl, out, 1000, s_ref=s_ref, scale=scale, label="zero-center")
 
 
-@pytest.mark.parametrize("long_len", [65536, 70000])
-def test_zero_center_large_tie_group(long_len):
-    """40000 tied keys: more candidates than the candidate buffer holds (the fallback path of the
-    split select); with units up to 65536 rows, the one-workgroup select on all-tied keys."""
+@pytest.mark.parametrize("long_len,max_rows", [(65536, None), (70000, None), (70000, SPLIT_ROWS)])
+def test_zero_center_large_tie_group(long_len, max_rows):
+    """40000 tied keys: more candidates than the candidate buffer holds (the paths that read the
+    scores again instead), in the fused resolve-and-emit kernel and in the resolve kernel."""
     wl = workload("c2")
     P = pack_units(wl, [0, 1, 2], [40000, 9000, long_len])
     centers = P["centers"].copy()
     centers[0] = 0.0
     centers[2] = 0.0
-    say(f"case zero center, 40000 and {long_len} ties")
+    say(f"case zero center, 40000 and {long_len} ties, max_rows={max_rows}")
     for path in ["fused", "calls"]:
-        out = run_gpu(P, wl, 2048, centers=centers, path=path)
+        out = run_gpu(P, wl, 2048, centers=centers, path=path, max_rows=max_rows)
         assert np.array_equal(out["kept_idx"][0], np.arange(2048))
         assert np.array_equal(out["kept_idx"][2], np.arange(2048))
         s_ref, scale = oracle_unit(P, 1, wl, centers=centers)
