@@ -10,8 +10,9 @@
 //     P = x cos(w Delta) - y sin(w Delta),  Q = x sin(w Delta) + y cos(w Delta)
 // (x, y as in the averaged score, with the raw center); then per offset the band's term is
 //     P cos(w delta) - Q sin(w delta),
-// two FMAs against a table of (cos, sin)(w_f delta) built in LDS once per workgroup. The 16
-// lanes of a row add each offset's terms with DPP and keep the running maximum.
+// two FMAs against a table of (cos, sin)(w_f delta) built in LDS once per workgroup. The lanes of
+// a row add each offset's terms with DPP and keep the running maximum; with 16 lanes per row
+// (d = 128) whole groups of 16 offsets are reduced together (a reduce-scatter across the lanes).
 #include "score_device.h"
 
 namespace tri {
@@ -25,10 +26,28 @@ using dev::order_key;
 using namespace sdev;
 
 constexpr int kMaxThreads = 256;
-constexpr int kMaxRowsPerLoad = 2;
+constexpr int kMaxRowsPerLoad = 4;
 
 template <int D>
 constexpr int max_rows_per_block() { return 256; }
+
+// This lane's four bands of one row at one offset: sum_j P_j cos(w_j delta) - Q_j sin(w_j delta),
+// with w01 = (cos, sin) of bands 0 and 1 and w23 of bands 2 and 3.
+__device__ __forceinline__ float band_terms(const float (&P)[4], const float (&Q)[4], const float4& w01,
+                                            const float4& w23) {
+  float v = fmaf(P[0], w01.x, -(Q[0] * w01.y));
+  v = fmaf(P[1], w01.z, fmaf(-Q[1], w01.w, v));
+  v = fmaf(P[2], w23.x, fmaf(-Q[2], w23.y, v));
+  return fmaf(P[3], w23.z, fmaf(-Q[3], w23.w, v));
+}
+
+// Maximum over each aligned group of 16 lanes; every lane gets it.
+__device__ __forceinline__ float group_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // lane ^ 1
+  v = fmaxf(v, dpp_f<0x4E>(v));   // lane ^ 2
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+}
 
 template <int DT, int LAYOUT, int D, bool HIST>
 __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int chunks_per_unit, BandConst bc,
@@ -115,12 +134,12 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
         pb[m] = load_pos(pbase, row);
       }
     }
-    float best[M];
+    // per row and band: the center term rotated by the distance, (P, Q)
+    float P[M][4], Q[M][4];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const uint32_t dl = (uint32_t)(t - pc[m]);
       const float df = (float)dl;
-      float P[4], Q[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float rev = band_phase(dl, df, step[j], resid[j]);
@@ -128,20 +147,51 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
         const float cs = __builtin_amdgcn_cosf(rev);
         float x, y;
         cc.xy(kc[m], j, x, y);
-        P[j] = fmaf(x, cs, -(y * sn));
-        Q[j] = fmaf(x, sn, y * cs);
+        P[m][j] = fmaf(x, cs, -(y * sn));
+        Q[m][j] = fmaf(x, sn, y * cs);
       }
-      float b = -__builtin_inff();
-      for (int o = 0; o < n_off; ++o) {
-        const float4 w01 = *reinterpret_cast<const float4*>(&tab[o][4 * l]);
-        const float4 w23 = *reinterpret_cast<const float4*>(&tab[o][4 * l + 2]);
-        float s = fmaf(P[0], w01.x, -(Q[0] * w01.y));
-        s = fmaf(P[1], w01.z, fmaf(-Q[1], w01.w, s));
-        s = fmaf(P[2], w23.x, fmaf(-Q[2], w23.y, s));
-        s = fmaf(P[3], w23.z, fmaf(-Q[3], w23.w, s));
-        b = fmaxf(b, group_sum<LPR>(s));
+    }
+    // offsets outer: one table read serves the M rows of this lane
+    float best[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) best[m] = -__builtin_inff();
+    int o0 = 0;
+    if constexpr (LPR == 16) {
+      // whole groups of 16 offsets: lane l's slot k holds offset 16c + ((k + l) mod 16), so that
+      // four row_ror steps (8, 4, 2, 1) leave in each lane the row sum of one offset, 15 DPP adds
+      // for 16 offsets instead of 64; the maximum over the lanes is taken once at the end.
+      for (; o0 + 16 <= n_off; o0 += 16) {
+        float acc[M][16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int o = o0 + ((k + l) & 15);
+          const float4 w01 = *reinterpret_cast<const float4*>(&tab[o][4 * l]);
+          const float4 w23 = *reinterpret_cast<const float4*>(&tab[o][4 * l + 2]);
+#pragma unroll
+          for (int m = 0; m < M; ++m) acc[m][k] = band_terms(P[m], Q[m], w01, w23);
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[m][k] += dpp_f<0x128>(acc[m][k + 8]);  // row_ror:8
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[m][k] += dpp_f<0x124>(acc[m][k + 4]);  // row_ror:4
+#pragma unroll
+          for (int k = 0; k < 2; ++k) acc[m][k] += dpp_f<0x122>(acc[m][k + 2]);  // row_ror:2
+          acc[m][0] += dpp_f<0x121>(acc[m][1]);                                  // row_ror:1
+          best[m] = fmaxf(best[m], acc[m][0]);
+        }
       }
-      best[m] = b;
+    }
+    for (int o = o0; o < n_off; ++o) {  // the rest one at a time, every lane gets the row sum
+      const float4 w01 = *reinterpret_cast<const float4*>(&tab[o][4 * l]);
+      const float4 w23 = *reinterpret_cast<const float4*>(&tab[o][4 * l + 2]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) best[m] = fmaxf(best[m], group_sum<LPR>(band_terms(P[m], Q[m], w01, w23)));
+    }
+    if constexpr (LPR == 16) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) best[m] = group_max16(best[m]);
     }
     if (l < M) {
       float v = best[0];
