@@ -1003,6 +1003,7 @@ hipError_t launch_move(const SelectArgs& a, const MoveArgs& mv, hipStream_t s) {
 constexpr int kTN = 1024;
 constexpr int kTW = kTN / 64;
 constexpr int64_t kTopbMaxRows = 64 * kTN;
+constexpr int kTopbMinUnits = 256;  // tri_select_topb and tri_prune_pass use it from this many units on
 
 struct TopbShared {
   uint32_t sh[4 * kTW];
@@ -1146,6 +1147,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   if (!a.hist_ready && hpu > 0)
     hipLaunchKernelGGL(hist_kernel, dim3((unsigned)(U * hpu)), dim3(kHN), 0, s, a, (int)hpu);
+  if (a.max_rows <= kTopbMaxRows && a.n_units >= kTopbMinUnits) {  // one workgroup per unit fills the GPU
+    hipError_t e = launch_topb<false>(a, InplaceOut{nullptr, nullptr, 0u}, s);
+    if (e != hipSuccess || a.K_out == nullptr) return e;
+    const CompactArgs c{a.K, a.V, a.pos, a.row_bytes, a.row_off, a.n_units, a.total_rows, a.kept_idx, a.kept_cnt,
+                        a.B, a.K_out, a.V_out, a.pos_out};
+    return launch_compact(c, s);
+  }
   hipLaunchKernelGGL(cand_kernel, dim3((unsigned)cand_grid), dim3(kCN), 0, s, a);
   if (a.max_rows <= kFinishMaxRows) {
     hipError_t e = hipSuccess;

@@ -98,6 +98,27 @@ def test_edge_cases_ragged_units(max_rows):
         assert out["ws_after"]
 
 
+def test_many_units_one_workgroup_select():
+    """264 ragged units (empty, one row, tails, up to 20000 rows): from 256 units on, the select
+    holds each unit's keys in one workgroup and the compaction runs as its own kernel. Its
+    results equal those of the fused resolve-and-emit path (max_rows above 64Ki) bit for bit,
+    and sampled units match the oracle."""
+    wl = workload("c2")
+    pattern = [0, 1, 5, 511, 512, 513, 2049, 4100, 20000, 300, 64]
+    lengths = pattern * 24
+    units = list(range(len(lengths)))
+    P = pack_units(dataclasses.replace(wl, heads=len(lengths)), units, lengths, workers=gen_workers())
+    for B in [0, 1, 300, 2048, 5000]:
+        say(f"case many units B={B}")
+        out = run_gpu(P, wl, B)
+        ref = run_gpu(P, wl, B, max_rows=65537)
+        for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
+            assert np.array_equal(out[k], ref[k]), (B, k)
+        assert out["ws_after"]
+        for i in [0, 1, 3, 8, 19, 263]:
+            check_unit(P, i, wl, out, B, label=f"many units B={B}")
+
+
 def test_all_units_empty():
     """No rows at all (zero-size inputs): every unit keeps nothing, outputs stay untouched."""
     wl = dataclasses.replace(workload("c2"), heads=3)
