@@ -205,9 +205,12 @@ int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, 
  *             of these scores (same row_off, max_rows) into ws
  *   stream    hipStream_t or NULL
  * Method: radix select of the B-th largest score per unit (12 + 10 + 10 bits), the last two
- *   digits resolved among the keys of the threshold's top-digit bin; then one ordered pass
- *   writes the kept indices. Every unit is split into workgroups of >= 1024 rows for the
- *   threshold and into granules of >= 64 rows for the output pass.
+ *   digits resolved among the keys of the threshold's top-digit bin; then the kept indices are
+ *   written in order. The arrangement depends on the shape, not the result: with fewer than
+ *   256 units of up to 2^18 rows, a candidate kernel (1024 rows per workgroup) and one kernel
+ *   that resolves the threshold and writes 64 output slots per workgroup; with 256 units or
+ *   more of up to 2^16 rows, one workgroup per unit; longer units take separate candidate,
+ *   threshold and output kernels.
  */
 int tri_select_topb(const float* scores, const int64_t* row_off, int n_units,
                     int64_t total_rows, int64_t max_rows, int B, int32_t* kept_idx,
@@ -240,9 +243,10 @@ int tri_compact_kv(const void* K, const void* V, const int32_t* pos, int dtype, 
                    void* V_out, int32_t* pos_out, void* stream);
 
 /*
- * tri_prune_pass - one whole pruning pass: tri_score, tri_select_topb and tri_compact_kv fused
- * into four launches (score with histogram; candidates; threshold; emit with the row gather),
- * same results as calling the three in turn.
+ * tri_prune_pass - one whole pruning pass: tri_score, tri_select_topb and tri_compact_kv fused,
+ * same results as calling the three in turn. Three launches for the common shapes (score with
+ * histogram; candidates; threshold with output and row gather, or for 256 units and more:
+ * score; select; row gather), four for units longer than 2^18 rows.
  *
  * Arguments are those of the three functions: K (the keys) and V as in tri_compact_kv, the
  * score arguments as in tri_score, B, kept_idx and kept_cnt as in tri_select_topb, K_out /
@@ -279,7 +283,8 @@ int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, d
  *   kept_cnt    device int32[n_units]: m_u
  *   ws, ws_bytes  workspace as in tri_select_topb, with its own size query (it also depends on B)
  *   stream      hipStream_t or NULL
- * Launches: score with histogram; candidates; threshold; freed-slot and mover lists; moves.
+ * Launches: score with histogram; threshold with the freed-slot and mover lists (one
+ * workgroup per unit, units up to 2^16 rows; longer: candidates, threshold, lists); moves.
  * No buffer may overlap another (TRI_ERR_ALIAS).
  */
 int tri_prune_inplace(void* K, void* V, int32_t* pos, int dtype, int layout, int d, double theta,

@@ -11,14 +11,28 @@
 // hist_kernel here), then bits 19..10 and 9..0 among the keys whose top digit is the threshold's
 // ("candidates"). Kept rows: key > T, and the `need` lowest-index rows with key == T.
 //
-// A unit's data is spread over many workgroups in every phase: one workgroup moves only a
-// fraction of the HBM bandwidth a CU can see, so a per-unit pass over 32k scores, or a dense
-// run of kept rows gathered by one workgroup, would set the time of the whole call.
+// Three arrangements of the same select, chosen on the host from the unit count and max_rows
+// (all give the same bits):
+//
+//  * Units of up to 2^18 rows, fewer than 256 units (one layer's heads):
+//      cand_kernel -> finish_kernel
+//    A unit is spread over many workgroups: one workgroup sees only a fraction of the HBM
+//    bandwidth and one CU's VALU, so a per-unit pass over 32k scores in one workgroup, or a
+//    dense run of kept rows gathered by one workgroup, would set the time of the whole call.
+//  * Units of up to 64Ki rows, 256 units or more (many layers in one call):
+//      topb_kernel -> compact_kernel
+//    One workgroup per unit with the keys in registers; the units alone fill the GPU.
+//  * Longer units: cand_kernel -> resolve_kernel -> emit_kernel.
+//  The in-place pass uses topb_kernel (up to 64Ki rows) or cand/resolve/mark_kernel, then
+//  move_kernel.
 //
 //  hist_kernel     (standalone select only) top-digit histogram, 4096 rows per workgroup.
 //  cand_kernel     256 threads per 1024 rows (or one granule, if larger): finds the threshold's
 //                  top digit b0 from the histogram, counts per granule the keys above it and
 //                  writes the workgroup's candidates, packed, to its own region.
+//  finish_kernel   one workgroup per 64 output slots: resolves digits 2 and 3 from the unit's
+//                  candidates itself, finds the granules whose kept rows land in its slots, and
+//                  writes and gathers those rows.
 //  resolve_kernel  one workgroup per unit: clears the histogram, stages the candidates in LDS,
 //                  resolves digits 2 and 3, and turns per-granule kept counts into per-granule
 //                  output offsets and counts of ties before each granule (block-wide DPP scans).
@@ -30,6 +44,8 @@
 //                  fused, a granule has a second wave: the first copies the kept K rows and the
 //                  positions, the second the V rows, up to 8 loads of 16 bytes per lane in flight
 //                  (a dense run of kept rows is spread over many waves, not one CU).
+//  topb_kernel     one 1024-thread workgroup per unit, all three digits over keys held in
+//                  registers; writes the kept indices (or the in-place lists) itself.
 #include "tri_device.h"
 
 namespace tri {
