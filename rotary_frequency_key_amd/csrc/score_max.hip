@@ -11,8 +11,8 @@
 // (x, y as in the averaged score, with the raw center); then per offset the band's term is
 //     P cos(w delta) - Q sin(w delta),
 // two FMAs against a table of (cos, sin)(w_f delta) built in LDS once per workgroup. The lanes of
-// a row add each offset's terms with DPP and keep the running maximum; with 16 lanes per row
-// (d = 128) whole groups of 16 offsets are reduced together (a reduce-scatter across the lanes).
+// a row add each offset's terms with DPP and keep the running maximum. For d = 128 the offset
+// loop is a matrix product instead and runs on the matrix cores (score_max_mfma_kernel).
 #include "score_device.h"
 
 namespace tri {
@@ -155,43 +155,11 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
     float best[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) best[m] = -__builtin_inff();
-    int o0 = 0;
-    if constexpr (LPR == 16) {
-      // whole groups of 16 offsets: lane l's slot k holds offset 16c + ((k + l) mod 16), so that
-      // four row_ror steps (8, 4, 2, 1) leave in each lane the row sum of one offset, 15 DPP adds
-      // for 16 offsets instead of 64; the maximum over the lanes is taken once at the end.
-      for (; o0 + 16 <= n_off; o0 += 16) {
-        float acc[M][16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int o = o0 + ((k + l) & 15);
-          const float4 w01 = *reinterpret_cast<const float4*>(&tab[o][4 * l]);
-          const float4 w23 = *reinterpret_cast<const float4*>(&tab[o][4 * l + 2]);
-#pragma unroll
-          for (int m = 0; m < M; ++m) acc[m][k] = band_terms(P[m], Q[m], w01, w23);
-        }
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) acc[m][k] += dpp_f<0x128>(acc[m][k + 8]);  // row_ror:8
-#pragma unroll
-          for (int k = 0; k < 4; ++k) acc[m][k] += dpp_f<0x124>(acc[m][k + 4]);  // row_ror:4
-#pragma unroll
-          for (int k = 0; k < 2; ++k) acc[m][k] += dpp_f<0x122>(acc[m][k + 2]);  // row_ror:2
-          acc[m][0] += dpp_f<0x121>(acc[m][1]);                                  // row_ror:1
-          best[m] = fmaxf(best[m], acc[m][0]);
-        }
-      }
-    }
-    for (int o = o0; o < n_off; ++o) {  // the rest one at a time, every lane gets the row sum
+    for (int o = 0; o < n_off; ++o) {
       const float4 w01 = *reinterpret_cast<const float4*>(&tab[o][4 * l]);
       const float4 w23 = *reinterpret_cast<const float4*>(&tab[o][4 * l + 2]);
 #pragma unroll
       for (int m = 0; m < M; ++m) best[m] = fmaxf(best[m], group_sum<LPR>(band_terms(P[m], Q[m], w01, w23)));
-    }
-    if constexpr (LPR == 16) {
-#pragma unroll
-      for (int m = 0; m < M; ++m) best[m] = group_max16(best[m]);
     }
     if (l < M) {
       float v = best[0];
@@ -215,6 +183,227 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// d = 128: the offset loop as a matrix product on the matrix cores
+// ---------------------------------------------------------------------------------------------
+//
+// For one row, S(delta_o) = sum_f P_f cos(w_f delta_o) - Q_f sin(w_f delta_o) is the product of
+// the row [P_0..P_63, Q_0..Q_63] with column o of W = [cos(w_f delta_o); -sin(w_f delta_o)]:
+// 16 rows x 128 x 16 offsets per v_mfma_f32_16x16x32_bf16 tile (K = 32 per instruction, four
+// steps). Each operand is split into bf16 hi + lo (x = hi + lo + O(2^-16 x)) and the product is
+// hi*hi + hi*lo + lo*hi, accumulated in fp32. A wave writes its 16 rows' P, Q (hi and lo) to an
+// LDS tile in the lane layout the instruction takes (lane L: row L % 16, k = 8 (L / 16) + i), and
+// holds W in registers for the whole workgroup. Offsets past the last repeat it (the maximum
+// does not change). The result tile gives lane L offset L % 16 of rows 4 (L / 16) + i; a DPP
+// maximum over the 16 lanes of each row group finishes the row.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4m __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaRowsPerBlock = 512;
+constexpr int kTileStride = 136;  // bf16 per LDS tile row: 128 + 8 (16 bytes of padding against bank conflicts)
+
+// x = hi + lo with hi, lo bf16 (round to nearest even both times)
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+template <int DT, int LAYOUT, bool HIST, int NT>  // NT: tiles of 16 offsets
+__global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a, int chunks_per_unit, BandConst bc,
+                                                                     OffsetSet os) {
+  constexpr int D = 128, F = 64, LPR = 16, GPW = 4, M = 4;
+  constexpr int ROWS_WAVE = GPW * M;  // 16: one matrix tile of rows
+  constexpr int WAVES = kMaxThreads / 64;
+  constexpr int ROWS_ITER = ROWS_WAVE * WAVES;
+  constexpr int RPB = kMfmaRowsPerBlock;
+  constexpr int ITERS = RPB / ROWS_ITER;
+  static_assert(RPB % ROWS_ITER == 0, "rows per block");
+  using L = RowLoad<DT, LAYOUT, D>;
+  using KT = typename L::T;
+
+  __shared__ __align__(16) float2 tab[kMaxOffsets][F];                  // (cos, sin)(omega_f delta)
+  __shared__ __align__(16) __bf16 tile[WAVES][2][ROWS_WAVE][kTileStride];  // per wave: hi, lo
+  __shared__ uint32_t lhist[HIST ? kHistBins : 1];
+
+  const int unit = blockIdx.x / chunks_per_unit;
+  const int chunk = blockIdx.x - unit * chunks_per_unit;
+  const dev::UnitRows ur = dev::unit_rows(a.row_off, unit, a.total_rows, a.max_rows);
+  const int64_t beg = ur.beg, end = ur.beg + ur.n;
+  const int64_t r0 = beg + (int64_t)chunk * RPB;
+  if (r0 >= end) return;
+  const int64_t r1 = (end - r0 < RPB) ? end : r0 + RPB;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l = lane % LPR;   // setup layout: bands 4l .. 4l+3 of rows m*GPW + gw
+  const int gw = lane / LPR;
+  const int mc = lane & 15;   // matrix layout: row (A) or offset column (B, result) ...
+  const int mq = lane >> 4;   // ... and k block 8*mq .. 8*mq+7
+  const int n_off = os.n;
+
+  const char* kbase = static_cast<const char*>(a.keys) + r0 * L::kRowBytes;
+  const int32_t* pbase = a.pos + r0;
+  const uint32_t last = (uint32_t)(r1 - r0 - 1);
+  const uint32_t wave_row = (uint32_t)(wave * ROWS_WAVE + gw);
+  KT kb[M];
+  int32_t pb[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint32_t row = min(wave_row + m * GPW, last);
+    kb[m] = L::load(kbase, row, l);
+    pb[m] = load_pos(pbase, row);
+  }
+
+  // the offset table, the histogram, and this lane's constants
+  for (int i = threadIdx.x; i < n_off * F; i += kMaxThreads) {
+    const int o = i / F, f = i - o * F;
+    const uint32_t dl = os.delta[o];
+    const float rev = band_phase(dl, (float)dl, bc.step[f] & 0x7FFFFFu, bc.resid[f]);
+    tab[o][f] = make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+  }
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < kHistBins; i += kMaxThreads) lhist[i] = 0u;
+  }
+  uint32_t step[4];
+  float resid[4];
+  float cre[4], cim[4];
+  {
+    const float4* mp = reinterpret_cast<const float4*>(a.mu + ((size_t)unit * F + 4 * l) * 2);
+    const float4 m0 = mp[0], m1 = mp[1];
+    cre[0] = m0.x; cim[0] = m0.y; cre[1] = m0.z; cim[1] = m0.w;
+    cre[2] = m1.x; cim[2] = m1.y; cre[3] = m1.z; cim[3] = m1.w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { step[j] = bc.step[4 * l + j] & 0x7FFFFFu; resid[j] = bc.resid[4 * l + j]; }
+  }
+  CenterCoef<DT> cc;
+  cc.init(cre, cim);
+  const int32_t t = a.t_now[unit];
+  __syncthreads();
+
+  // W in registers: tile tt, step s: column o = 16 tt + mc (the last offset past n_off), rows
+  // k = 32 s + 8 mq + i: cos(w_k delta_o) for k < 64, -sin(w_{k-64} delta_o) above
+  bf16x8 whi[NT][4], wlo[NT][4];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int o = min(16 * tt + mc, n_off - 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = 32 * s + 8 * mq + i;
+        const float2 cs = tab[o][k & 63];
+        __bf16 h, lo;
+        split_bf16(k < 64 ? cs.x : -cs.y, h, lo);
+        whi[tt][s][i] = h;
+        wlo[tt][s][i] = lo;
+      }
+    }
+  }
+
+  __bf16* th = &tile[wave][0][0][0];
+  __bf16* tl = &tile[wave][1][0][0];
+  for (int it = 0; it < ITERS; ++it) {
+    KT kc[M];
+    int32_t pc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) { kc[m] = kb[m]; pc[m] = pb[m]; }
+    const uint32_t base = (uint32_t)(it * ROWS_ITER + wave * ROWS_WAVE);  // the wave's first row
+    if (it + 1 < ITERS) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint32_t row = min(wave_row + (uint32_t)((it + 1) * ROWS_ITER) + m * GPW, last);
+        kb[m] = L::load(kbase, row, l);
+        pb[m] = load_pos(pbase, row);
+      }
+    }
+    // per row and band: (P, Q), split, into the wave's tile (row m*GPW + gw; k = 4l + j, 64 + 4l + j)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint32_t dl = (uint32_t)(t - pc[m]);
+      const float df = (float)dl;
+      __bf16 ph[4], pl[4], qh[4], ql[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float rev = band_phase(dl, df, step[j], resid[j]);
+        const float sn = __builtin_amdgcn_sinf(rev);
+        const float cs = __builtin_amdgcn_cosf(rev);
+        float x, y;
+        cc.xy(kc[m], j, x, y);
+        split_bf16(fmaf(x, cs, -(y * sn)), ph[j], pl[j]);
+        split_bf16(fmaf(x, sn, y * cs), qh[j], ql[j]);
+      }
+      const int rr = m * GPW + gw;
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<bf16x4*>(th + rr * kTileStride + 4 * l) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
+      *reinterpret_cast<bf16x4*>(th + rr * kTileStride + 64 + 4 * l) = bf16x4{qh[0], qh[1], qh[2], qh[3]};
+      *reinterpret_cast<bf16x4*>(tl + rr * kTileStride + 4 * l) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
+      *reinterpret_cast<bf16x4*>(tl + rr * kTileStride + 64 + 4 * l) = bf16x4{ql[0], ql[1], ql[2], ql[3]};
+    }
+    // the tile is this wave's own: its LDS operations run in order; keep the compiler's order too
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    f32x4m acc[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4m{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(th + mc * kTileStride + 32 * s + 8 * mq);
+      const bf16x8 alo = *reinterpret_cast<const bf16x8*>(tl + mc * kTileStride + 32 * s + 8 * mq);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, whi[tt][s], acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, wlo[tt][s], acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, whi[tt][s], acc[tt], 0, 0, 0);
+      }
+    }
+    // the next iteration rewrites the tile only after these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane L: offset column mc of rows 4 mq + i; maximum over the offsets, then over the 16 lanes
+    float best[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[0][i];
+#pragma unroll
+      for (int tt = 1; tt < NT; ++tt) v = fmaxf(v, acc[tt][i]);
+      best[i] = group_max16(v);
+    }
+    if (mc < 4) {
+      const float v = mc == 0 ? best[0] : mc == 1 ? best[1] : mc == 2 ? best[2] : best[3];
+      const uint32_t row = base + 4 * mq + mc;
+      if (row <= last) {
+        a.scores[r0 + row] = v;
+        if constexpr (HIST) atomicAdd(&lhist[order_key(v) >> kHistShift], 1u);
+      }
+    }
+  }
+
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* gh = a.hist + (size_t)unit * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += kMaxThreads) {
+      const uint32_t c = lhist[i];
+      if (c) atomicAdd(&gh[i], c);
+    }
+  }
+}
+
+template <int DT, int LAYOUT, int NT>
+hipError_t launch_mfma(const ScoreArgs& a, const BandConst& bc, const OffsetSet& os, hipStream_t s) {
+  constexpr int RPB = kMfmaRowsPerBlock;
+  const int64_t chunks = (a.max_rows + RPB - 1) / RPB;
+  const int64_t grid = chunks * a.n_units;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid), b(kMaxThreads);
+  if (a.hist) hipLaunchKernelGGL((score_max_mfma_kernel<DT, LAYOUT, true, NT>), g, b, 0, s, a, (int)chunks, bc, os);
+  else hipLaunchKernelGGL((score_max_mfma_kernel<DT, LAYOUT, false, NT>), g, b, 0, s, a, (int)chunks, bc, os);
+  return hipGetLastError();
+}
+
 template <int DT, int LAYOUT, int D>
 hipError_t launch_t(const ScoreArgs& a, const BandConst& bc, const OffsetSet& os, hipStream_t s) {
   constexpr int RPB = max_rows_per_block<D>();
@@ -232,7 +421,8 @@ template <int DT, int LAYOUT>
 hipError_t launch_d(const ScoreArgs& a, const BandConst& bc, const OffsetSet& os, hipStream_t s) {
   switch (a.d) {
     case 64: return launch_t<DT, LAYOUT, 64>(a, bc, os, s);
-    case 128: return launch_t<DT, LAYOUT, 128>(a, bc, os, s);
+    case 128:  // the matrix-core form
+      return os.n <= 16 ? launch_mfma<DT, LAYOUT, 1>(a, bc, os, s) : launch_mfma<DT, LAYOUT, 2>(a, bc, os, s);
     case 256: return launch_t<DT, LAYOUT, 256>(a, bc, os, s);
     default: return hipErrorInvalidValue;
   }

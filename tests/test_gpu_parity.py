@@ -280,10 +280,13 @@ def test_rotated_keys(dtype, layout):
     assert np.array_equal(alone.cpu().numpy(), out["scores"])
 
 
-@pytest.mark.parametrize("d,dtype,layout", [(128, "bf16", 0), (128, "bf16", 1), (64, "f32", 0), (256, "bf16", 0)])
+@pytest.mark.parametrize("d,dtype,layout", [(128, "bf16", 0), (128, "bf16", 1), (128, "f32", 0), (64, "f32", 0),
+                                             (256, "bf16", 0)])
 def test_max_over_offsets(d, dtype, layout):
     """The maximum over the offsets of the unfolded score, against the oracle's literal loop; then
-    the select and the compaction on its histogram (score_max -> select -> compact)."""
+    the select and the compaction on its histogram (score_max -> select -> compact). d = 128 runs
+    on the matrix cores: 17 offsets (one full tile of 16 and one padded), 5 (one padded tile) and
+    32 (two full tiles)."""
     import rotary_frequency_key_amd as tri
 
     wl = dataclasses.replace(workload("c2"), d=d, dtype=dtype, heads=3, theta=5e5)
@@ -299,7 +302,10 @@ def test_max_over_offsets(d, dtype, layout):
     dev = torch.device("cuda:0")
     from tests._parity import keys_to_device, keys_to_host
     U, B = 3, 500
-    for offsets in [O.power_of_two_offsets(), np.array([0, 3, 17, 1000, 99991], dtype=np.int64)]:
+    sets = [O.power_of_two_offsets(), np.array([0, 3, 17, 1000, 99991], dtype=np.int64)]
+    if d == 128:
+        sets.append(np.arange(32, dtype=np.int64) * 977 + 5)
+    for offsets in sets:
         say(f"case max over offsets d={d} {dtype} layout={layout} |D|={offsets.size}")
         K = keys_to_device(keys, dtype, dev)
         V = keys_to_device(P["values"], dtype, dev)
