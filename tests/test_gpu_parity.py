@@ -115,6 +115,12 @@ def test_many_units_one_workgroup_select():
         for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
             assert np.array_equal(out[k], ref[k]), (B, k)
         assert out["ws_after"]
+        if B in (1, 2048):  # the three calls, and the standalone select with its own histogram
+            for path in ["calls", "standalone"]:
+                o2 = run_gpu(P, wl, B, path=path)
+                for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
+                    assert np.array_equal(o2[k], out[k]), (B, path, k)
+                assert o2["ws_after"], (B, path)
         for i in [0, 1, 3, 8, 19, 263]:
             check_unit(P, i, wl, out, B, label=f"many units B={B}")
 
