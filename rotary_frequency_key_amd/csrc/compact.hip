@@ -18,12 +18,13 @@ __global__ __launch_bounds__(kNT) void compact_kernel(CompactArgs a, int blocks_
   const int u = blockIdx.x / blocks_per_unit;
   const int b = blockIdx.x - u * blocks_per_unit;
   const dev::UnitRows ur = dev::unit_rows(a.row_off, u, a.total_rows, a.total_rows);
-  int cnt = a.kept_cnt[u];
-  cnt = cnt < 0 ? 0 : (cnt > a.B ? a.B : cnt);
   const int j = b * ROWS + (int)threadIdx.x / CPR;
   const int part = (int)threadIdx.x % CPR;
+  // the count and the index are read together (slot j < B is always in range)
+  const int32_t src = a.kept_idx[(int64_t)u * a.B + (j < a.B ? j : a.B - 1)];
+  int cnt = a.kept_cnt[u];
+  cnt = cnt < 0 ? 0 : (cnt > a.B ? a.B : cnt);
   if (j >= cnt) return;
-  const int32_t src = a.kept_idx[(int64_t)u * a.B + j];
   if (src < 0 || src >= ur.n) return;
   const int64_t srow = ur.beg + src;
   const int64_t drow = (int64_t)u * a.B + j;
