@@ -203,10 +203,20 @@ typedef float f32x4m __attribute__((ext_vector_type(4)));
 constexpr int kMfmaRowsPerBlock = 512;
 constexpr int kTileStride = 136;  // bf16 per LDS tile row: 128 + 8 (16 bytes of padding against bank conflicts)
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2m __attribute__((ext_vector_type(2)));
+
 // x = hi + lo with hi, lo bf16 (round to nearest even both times)
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   hi = (__bf16)x;
   lo = (__bf16)(x - (float)hi);
+}
+// the same for a pair (one packed conversion each for hi and lo)
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, bf16x2& hi, bf16x2& lo) {
+  const f32x2m v = {x0, x1};
+  hi = __builtin_convertvector(v, bf16x2);
+  lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x2m), bf16x2);
 }
 
 template <int DT, int LAYOUT, bool HIST, int NT>  // NT: tiles of 16 offsets
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a
     for (int m = 0; m < M; ++m) {
       const uint32_t dl = (uint32_t)(t - pc[m]);
       const float df = (float)dl;
-      __bf16 ph[4], pl[4], qh[4], ql[4];
+      float P[4], Q[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float rev = band_phase(dl, df, step[j], resid[j]);
@@ -330,15 +340,19 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a
         const float cs = __builtin_amdgcn_cosf(rev);
         float x, y;
         cc.xy(kc[m], j, x, y);
-        split_bf16(fmaf(x, cs, -(y * sn)), ph[j], pl[j]);
-        split_bf16(fmaf(x, sn, y * cs), qh[j], ql[j]);
+        P[j] = fmaf(x, cs, -(y * sn));
+        Q[j] = fmaf(x, sn, y * cs);
       }
+      bf16x2 ph0, ph1, pl0, pl1, qh0, qh1, ql0, ql1;
+      split_bf16x2(P[0], P[1], ph0, pl0);
+      split_bf16x2(P[2], P[3], ph1, pl1);
+      split_bf16x2(Q[0], Q[1], qh0, ql0);
+      split_bf16x2(Q[2], Q[3], qh1, ql1);
       const int rr = m * GPW + gw;
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      *reinterpret_cast<bf16x4*>(th + rr * kTileStride + 4 * l) = bf16x4{ph[0], ph[1], ph[2], ph[3]};
-      *reinterpret_cast<bf16x4*>(th + rr * kTileStride + 64 + 4 * l) = bf16x4{qh[0], qh[1], qh[2], qh[3]};
-      *reinterpret_cast<bf16x4*>(tl + rr * kTileStride + 4 * l) = bf16x4{pl[0], pl[1], pl[2], pl[3]};
-      *reinterpret_cast<bf16x4*>(tl + rr * kTileStride + 64 + 4 * l) = bf16x4{ql[0], ql[1], ql[2], ql[3]};
+      *reinterpret_cast<bf16x4*>(th + rr * kTileStride + 4 * l) = bf16x4{ph0[0], ph0[1], ph1[0], ph1[1]};
+      *reinterpret_cast<bf16x4*>(th + rr * kTileStride + 64 + 4 * l) = bf16x4{qh0[0], qh0[1], qh1[0], qh1[1]};
+      *reinterpret_cast<bf16x4*>(tl + rr * kTileStride + 4 * l) = bf16x4{pl0[0], pl0[1], pl1[0], pl1[1]};
+      *reinterpret_cast<bf16x4*>(tl + rr * kTileStride + 64 + 4 * l) = bf16x4{ql0[0], ql0[1], ql1[0], ql1[1]};
     }
     // the tile is this wave's own: its LDS operations run in order; keep the compiler's order too
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
