@@ -325,7 +325,7 @@ def _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, ke
 def prune_pass(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=None, scores=None,
                kept_idx=None, kept_cnt=None, K_out=None, V_out=None, pos_out=None,
                layout=TRI_BANDS_INTERLEAVED):
-    """One pruning pass through tri_prune_pass (score, select and compaction, four launches).
+    """One pruning pass through tri_prune_pass (score, select and compaction, three launches).
     Returns (scores, kept_idx, kept_cnt, K_out, V_out, pos_out)."""
     tensors, nbytes, args = _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores,
                                        kept_idx, kept_cnt, K_out, V_out, pos_out, layout)
