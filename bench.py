@@ -4,10 +4,10 @@
 A step is one pass over the Qwen3-8B-shaped layer workload (8 KV heads x 32768 bf16 keys,
 d = 128, theta = 1e6, offsets 2^0..2^16, B = 2048): one tri_prune_pass call (score with the
 fused radix histogram, candidates, then threshold, output slots and row gather in one kernel), on
-the current stream. Inputs are resident in HBM; to keep the 256 MB Infinity Cache from serving them, consecutive steps rotate over
-``--rotate`` distinct copies of the inputs and outputs (about 135 MB per copy), and the score
-kernel alone rotates over at least 8 copies of the keys (67 MB each): with 4 copies or fewer it
-runs measurably faster, served in part from the Infinity Cache.
+the current stream. Inputs are resident in HBM; to keep the 256 MB Infinity Cache from serving
+them, consecutive steps rotate over ``--rotate`` distinct copies of the inputs and outputs (about
+135 MB per copy), and the score kernel alone rotates over at least 8 copies of the keys (67 MB
+each): with 4 copies or fewer it runs measurably faster, served in part from the Infinity Cache.
 
 Prints ONE JSON line (rank 0). Extra legs:
   --pmc-copy       only run a plain device copy of known size (for counter calibration)
