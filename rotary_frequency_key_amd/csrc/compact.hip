@@ -28,11 +28,14 @@ __global__ __launch_bounds__(kNT) void compact_kernel(CompactArgs a, int blocks_
   if (src < 0 || src >= ur.n) return;
   const int64_t srow = ur.beg + src;
   const int64_t drow = (int64_t)u * a.B + j;
+  // every load before the stores: a load issued after a store waits for that store too
+  const bool with_pos = part == 0 && a.pos_out != nullptr;
   const uint4 kv = static_cast<const uint4*>(a.K)[srow * CPR + part];
   const uint4 vv = static_cast<const uint4*>(a.V)[srow * CPR + part];
+  const int32_t pv = with_pos ? a.pos[srow] : 0;
   static_cast<uint4*>(a.K_out)[drow * CPR + part] = kv;
   static_cast<uint4*>(a.V_out)[drow * CPR + part] = vv;
-  if (part == 0 && a.pos_out) a.pos_out[drow] = a.pos[srow];
+  if (with_pos) a.pos_out[drow] = pv;
 }
 
 template <int CPR>

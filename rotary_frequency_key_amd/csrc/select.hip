@@ -986,11 +986,15 @@ __global__ __launch_bounds__(256) void move_kernel(SelectArgs a, MoveArgs mv, in
   const uint32_t src = mv.mover[(size_t)u * mv.hcap + j];
   if (dst >= ur.n || src >= ur.n) return;  // only with an inconsistent workspace
   const int64_t sp = (ur.beg + src) * CPR + part, dp = (ur.beg + dst) * CPR + part;
+  // every load before the stores (a load issued after a store waits for that store too); the
+  // source rows (at or beyond m) and the destinations (below m) are disjoint
+  const bool with_pos = part == 0 && mv.pos != nullptr;
   const uint4 kv = static_cast<const uint4*>(mv.K)[sp];
   const uint4 vv = static_cast<const uint4*>(mv.V)[sp];
+  const int32_t pv = with_pos ? mv.pos[ur.beg + src] : 0;
   static_cast<uint4*>(mv.K)[dp] = kv;
   static_cast<uint4*>(mv.V)[dp] = vv;
-  if (part == 0 && mv.pos) mv.pos[ur.beg + dst] = mv.pos[ur.beg + src];
+  if (with_pos) mv.pos[ur.beg + dst] = pv;
 }
 
 template <int CPR>
