@@ -14,15 +14,16 @@
 // Three arrangements of the same select, chosen on the host from the unit count and max_rows
 // (all give the same bits):
 //
-//  * Units of up to 2^18 rows, fewer than 256 units (one layer's heads):
+//  * Units of up to 64Ki rows, 256 units or more (many layers in one call):
+//      topb_kernel -> compact_kernel
+//    One workgroup per unit with the keys in registers; the units alone fill the GPU.
+//  * Otherwise, units of up to 2^18 rows whose output slots make at most kFinishMaxWorkgroups
+//    groups of 64 in all (one layer's heads, budgets of a few thousand):
 //      cand_kernel -> finish_kernel
 //    A unit is spread over many workgroups: one workgroup sees only a fraction of the HBM
 //    bandwidth and one CU's VALU, so a per-unit pass over 32k scores in one workgroup, or a
 //    dense run of kept rows gathered by one workgroup, would set the time of the whole call.
-//  * Units of up to 64Ki rows, 256 units or more (many layers in one call):
-//      topb_kernel -> compact_kernel
-//    One workgroup per unit with the keys in registers; the units alone fill the GPU.
-//  * Longer units: cand_kernel -> resolve_kernel -> emit_kernel.
+//  * Everything else (longer units, or many slots): cand_kernel -> resolve_kernel -> emit_kernel.
 //  The in-place pass uses topb_kernel (up to 64Ki rows) or cand/resolve/mark_kernel, then
 //  move_kernel.
 //
@@ -480,6 +481,12 @@ __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
 
 constexpr int64_t kFinishMaxRows = int64_t(1) << 18;  // 64-row granules, at most 256 candidate workgroups
 constexpr int kFinSlots = 64;                         // output slots per workgroup
+// Every finish workgroup resolves its unit's threshold again. Used while its whole grid is about
+// two waves of the GPU's workgroups (256 CUs, one 1024-thread workgroup each): beyond that the
+// repeated resolves cost more than the separate resolve kernel's boundary. (2048 units of 132096
+// rows with B = 12000 would make 188 finish workgroups per unit: the pass took 33.1 ms with
+// them, 17.1 ms with candidates, resolve and emit.)
+constexpr int64_t kFinishMaxWorkgroups = 512;
 constexpr int kFinMaxCandWgs = kFinishMaxRows >> kCandRowsShift;
 
 struct FinShared {
@@ -1175,7 +1182,9 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
     return launch_compact(c, s);
   }
   hipLaunchKernelGGL(cand_kernel, dim3((unsigned)cand_grid), dim3(kCN), 0, s, a);
-  if (a.max_rows <= kFinishMaxRows) {
+  const int64_t mm = a.B < a.max_rows ? a.B : a.max_rows;
+  const int64_t fin_wgs = (int64_t)a.n_units * (mm > 0 ? (mm + kFinSlots - 1) / kFinSlots : 1);
+  if (a.max_rows <= kFinishMaxRows && fin_wgs <= kFinishMaxWorkgroups) {
     hipError_t e = hipSuccess;
     switch (a.K_out == nullptr ? 0 : a.row_bytes / 16) {
       case 0: e = launch_finish<0>(a, s); break;
