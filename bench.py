@@ -12,6 +12,8 @@ each): with 4 copies or fewer it runs measurably faster, served in part from the
 Prints ONE JSON line (rank 0). Extra legs:
   --pmc-copy       only run a plain device copy of known size (for counter calibration)
   --no-cpu         skip the CPU baseline
+  --no-large       skip the large device-generated workloads (all layers, ragged batch, chat pass 0)
+  --no-steady      skip the chat steady state
 """
 import argparse
 import hashlib
@@ -115,7 +117,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-copy", action="store_true")
     ap.add_argument("--no-steady", action="store_true")
-    ap.add_argument("--no-all-layers", action="store_true")
+    ap.add_argument("--no-large", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -378,9 +380,10 @@ def main():
     # free the pass copies before the larger caches
     del copies, plans
     torch.cuda.empty_cache()
-    if not args.no_all_layers:
-        result["all_layers"] = all_layers(tri, torch, dev, args)
-        torch.cuda.empty_cache()
+    if not args.no_large:
+        for name in LARGE_WORKLOADS:
+            result[name] = large_workload(tri, torch, dev, args, name)
+            torch.cuda.empty_cache()
     if not args.no_steady:
         result["steady_state"] = steady_state(tri, torch, dev, args)
     if not args.no_cpu:
@@ -388,16 +391,26 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def all_layers(tri, torch, dev, args):
-    """All 36 layers of the Qwen3-8B shape in one call: 288 units of 32768 bf16 keys (2.4 GB of K),
-    B = 2048, with 10% of the heads flat (near-zero query center, wide key noise). One
-    tri_prune_pass prunes every layer; with 256 units or more the select holds each unit in one
-    workgroup. Generated on the device (synthgen.device: the host recipe's centers, device-drawn
-    noise). 2.9 GB per pass, far beyond the 256 MB Infinity Cache, so no copies rotate."""
+# Large workloads, each in one tri_prune_pass call, generated on the device (synthgen.device: the
+# host recipe's centers, device-drawn noise). Each moves gigabytes per pass, far beyond the
+# 256 MB Infinity Cache, so no copies rotate.
+LARGE_WORKLOADS = {
+    "all_layers": ("c3", "36 layers x 8 KV heads x 32768 keys (Qwen3-8B shape), bf16, B=2048, "
+                         "10% flat heads; 256 units or more: one select workgroup per unit"),
+    "ragged_batch": ("c4", "16 sequences x 32 layers x 8 KV heads (Llama-3-8B shape), 8192..65536 keys "
+                           "per sequence, bf16, B=2048"),
+    "chat_pass0": ("c5", "4 sequences x 64 layers x 8 KV heads (Qwen3-32B shape), 131072 + 1024 keys, "
+                         "bf16, B=12000: candidates, resolve and emit"),
+}
+
+
+def large_workload(tri, torch, dev, args, name):
+    """One large workload: the pass and the score kernel alone, in keys/s and algorithmic GB/s."""
     from synthgen import workload
     from synthgen.device import device_workload
 
-    wl = workload("c3")
+    wl_name, note = LARGE_WORKLOADS[name]
+    wl = workload(wl_name)
     W = device_workload(wl, dev)
     U = wl.n_units
     R = int(W["row_off"][-1])
@@ -434,14 +447,13 @@ def all_layers(tri, torch, dev, args):
     alg_total = sum(alg.values())
     us, score_us = times
     del W, plan, splan, ws, ws_s, scores, outs
-    return {"workload": "36 layers x 8 KV heads x 32768 keys (Qwen3-8B shape), bf16, B=2048, 10% flat heads",
-            "units": U, "keys": R, "us_per_pass": us, "keys_per_s": R / (us * 1e-6),
+    return {"workload": note, "units": U, "keys": R, "us_per_pass": us, "keys_per_s": R / (us * 1e-6),
             "algorithmic_bytes_per_pass": alg_total,
             "hbm_gbps": alg_total / (us * 1e-6) / 1e9,
             "hbm_frac_of_peak": alg_total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
             "score_kernel_us": score_us,
             "score_kernel_gbps": (alg["K"] + alg["pos"]) / (score_us * 1e-6) / 1e9,
-            "note": "one tri_prune_pass for all layers; generated on the device"}
+            "note": "one tri_prune_pass; generated on the device"}
 
 
 def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
