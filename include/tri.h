@@ -208,7 +208,7 @@ int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, 
  *   digits resolved among the keys of the threshold's top-digit bin; then the kept indices are
  *   written in order. The arrangement depends on the shape, not the result: with 256 units or
  *   more of up to 2^16 rows, one workgroup per unit; otherwise, with units of up to 2^18 rows
- *   and at most 512 groups of 64 output slots in all (n_units * ceil(min(B, max_rows) / 64)), a
+ *   and at most 4096 groups of 64 output slots in all (n_units * ceil(min(B, max_rows) / 64)), a
  *   candidate kernel (1024 rows per workgroup) and one kernel that resolves the threshold and
  *   writes 64 output slots per workgroup; every other shape takes separate candidate,
  *   threshold and output kernels.

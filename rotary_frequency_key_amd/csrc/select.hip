@@ -18,7 +18,7 @@
 //      topb_kernel -> compact_kernel
 //    One workgroup per unit with the keys in registers; the units alone fill the GPU.
 //  * Otherwise, units of up to 2^18 rows whose output slots make at most kFinishMaxWorkgroups
-//    groups of 64 in all (one layer's heads, budgets of a few thousand):
+//    groups of 64 in all (a few layers' heads, budgets of a few thousand):
 //      cand_kernel -> finish_kernel
 //    A unit is spread over many workgroups: one workgroup sees only a fraction of the HBM
 //    bandwidth and one CU's VALU, so a per-unit pass over 32k scores in one workgroup, or a
@@ -481,12 +481,13 @@ __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
 
 constexpr int64_t kFinishMaxRows = int64_t(1) << 18;  // 64-row granules, at most 256 candidate workgroups
 constexpr int kFinSlots = 64;                         // output slots per workgroup
-// Every finish workgroup resolves its unit's threshold again. Used while its whole grid is about
-// two waves of the GPU's workgroups (256 CUs, one 1024-thread workgroup each): beyond that the
-// repeated resolves cost more than the separate resolve kernel's boundary. (2048 units of 132096
-// rows with B = 12000 would make 188 finish workgroups per unit: the pass took 33.1 ms with
-// them, 17.1 ms with candidates, resolve and emit.)
-constexpr int64_t kFinishMaxWorkgroups = 512;
+// Every finish workgroup resolves its unit's threshold again; beyond about 4096 finish
+// workgroups in all the repeated resolves cost more than the separate resolve kernel and its
+// boundary. Measured crossovers: units of 32768 rows with B = 2048 (32 finish workgroups per
+// unit): equal at 64-128 units, 2% slower at 255; units of 132096 rows with B = 12000 (188 per
+// unit): equal at 16 units, 10% slower at 32. 2048 of those units took 33.1 ms per pass with
+// finish_kernel and 17.1 ms with candidates, resolve and emit.
+constexpr int64_t kFinishMaxWorkgroups = 4096;
 constexpr int kFinMaxCandWgs = kFinishMaxRows >> kCandRowsShift;
 
 struct FinShared {
