@@ -288,7 +288,6 @@ __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
   const uint32_t b0 = st->b0, above0 = st->above0;
   const uint32_t ngu = ((n - 1) >> gshift) + 1;  // granules of this unit
   const uint32_t nwg = ((n - 1) >> cshift) + 1;  // candidate workgroups of this unit
-  const float* s = a.scores + ur.beg;
   const uint32_t* cin = w.cand + (((size_t)u * WPU) << cshift);
 
   // loads: this thread's granules and candidate workgroups 4t..4t+3, and its share of the
@@ -409,30 +408,45 @@ __global__ __launch_bounds__(kRN) void resolve_kernel(SelectArgs a) {
       }
     }
   } else {
-    // ---- more candidates than LDS holds: digits 2 and 3 and the per-granule counts from the
-    // scores themselves
-    pre = b0;
+    // ---- more candidates than LDS holds: three passes over the candidate words in the
+    // workspace (digit 2, digit 3, then the per-granule counts), each thread over the same share
+    // as above, the preloaded first ones from registers
+    auto each_cand = [&](auto&& f) {
+      if (tpw) {
+        if (cw < nwg) {
+          const uint32_t cnt_w = L.wgoff[cw + 1] - L.wgoff[cw];
 #pragma unroll
-    for (int digit = 0; digit < 2; ++digit) {
-      const int sh = digit == 0 ? 10 : 0;
-      uint32_t* rh = L.rhist[digit];
-      for (uint32_t i = threadIdx.x; i < n; i += kRN) {
-        const uint32_t kk = order_key(load_at(s, i));
-        if ((kk >> (sh + 10)) == pre) atomicAdd(&rh[(kk >> sh) & 1023u], 1u);
+          for (int k = 0; k < kPre; ++k)
+            if (ci + k * tpw < cnt_w) f(pv[k]);
+          for (uint32_t i = tpw * kPre + ci; i < cnt_w; i += tpw) f(cin[((size_t)cw << cshift) + i]);
+        }
+      } else {
+        for (uint32_t c = threadIdx.x; c < nwg; c += kRN) {
+          const uint32_t cnt_w = L.wgoff[c + 1] - L.wgoff[c];
+          for (uint32_t i = 0; i < cnt_w; ++i) f(cin[((size_t)c << cshift) + i]);
+        }
       }
-      __syncthreads();
-      const uint32_t v[1] = {rh[1023 - threadIdx.x]};
-      uint32_t above;
-      const uint32_t b = block_find<kRN, 1>(v, 1024, r, L.sh, L.found, &above);
-      r -= above;
-      pre = (pre << 10) | b;
-    }
-    T = pre;
+    };
+    each_cand([&](uint32_t p) { atomicAdd(&L.rhist[0][cand_d2(p)], 1u); });
+    __syncthreads();
+    uint32_t above;
+    const uint32_t v2[1] = {L.rhist[0][1023 - threadIdx.x]};
+    const uint32_t d2 = block_find<kRN, 1>(v2, 1024, r, L.sh, L.found, &above);
+    r -= above;
+    each_cand([&](uint32_t p) {
+      if (cand_d2(p) == d2) atomicAdd(&L.rhist[1][cand_d3(p)], 1u);
+    });
+    __syncthreads();
+    const uint32_t v3[1] = {L.rhist[1][1023 - threadIdx.x]};
+    const uint32_t d3 = block_find<kRN, 1>(v3, 1024, r, L.sh, L.found, &above);
+    r -= above;
+    T = (((b0 << 10) | d2) << 10) | d3;
     need = r;
-    for (uint32_t i = threadIdx.x; i < n; i += kRN) {
-      const uint32_t kk = order_key(load_at(s, i));
-      if ((kk >> kHistShift) == b0 && kk >= T) atomicAdd(&L.cnt[i >> gshift], kk > T ? 1u : 0x10000u);
-    }
+    const uint32_t lowT = T & 0xFFFFFu;
+    each_cand([&](uint32_t p) {
+      const uint32_t lk = p >> 12;
+      if (lk >= lowT) atomicAdd(&L.cnt[p & 0xFFFu], lk > lowT ? 1u : 0x10000u);
+    });
   }
   __syncthreads();
 

@@ -16,7 +16,8 @@ constexpr int kHistShift = 20;
 // max_rows rows has at most kMaxGran of them); the emit kernel gives each granule one wave. The
 // candidate kernel gives each workgroup 2^cand_shift rows (max(1024, granule)) and collects the
 // keys whose top digit is the threshold's ("candidates"); the resolve kernel stages up to
-// kCandCap of them in LDS (beyond that it reads the scores again). Per-granule counts are kept
+// kCandCap of them in LDS (beyond that it reads them from the workspace once per pass over
+// them). Per-granule counts are kept
 // in 16 bits, so granules are at most 2^15 rows and units at most kMaxSelectRows rows.
 constexpr int kGranMinShift = 6;
 constexpr int kMaxGran = 4096;

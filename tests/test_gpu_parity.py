@@ -212,6 +212,33 @@ def test_dense_candidate_workgroup(max_rows):
         assert tied == list(range(5000, 5000 + len(tied))), "ties keep the lowest rows"
 
 
+@pytest.mark.parametrize("max_rows", [None, SPLIT_ROWS])
+def test_candidate_overflow_spread_digits(max_rows):
+    """Keys near one common key and one position crowd 60000 scores into a few top-digit bins:
+    up to 13571 candidates, more than LDS holds, with digits 2 and 3 spread (the passes over
+    the stored candidate words), and up to 277 candidates in one candidate workgroup (past the
+    preloaded share)."""
+    from synthgen import f32_to_bf16_bits
+
+    wl = dataclasses.replace(workload("c2"), heads=2)
+    P = pack_units(wl, [0, 1], [60000, 5000])
+    rng = np.random.default_rng(41)
+    k0 = rng.standard_normal(wl.d)
+    P["keys"] = f32_to_bf16_bits((k0[None, :] + 0.05 * rng.standard_normal(P["keys"].shape)).astype(np.float32))
+    P["pos"] = np.zeros_like(P["pos"])  # one distance: scores depend on the key only
+    refs = [oracle_unit(P, i, wl) for i in range(2)]
+    for B in [3000, 12000, 20000]:
+        for path in ["fused", "calls"]:
+            say(f"case candidate overflow B={B} {path} max_rows={max_rows}")
+            out = run_gpu(P, wl, B, path=path, max_rows=max_rows)
+            for i in range(2):
+                check_unit(P, i, wl, out, B, s_ref=refs[i][0], scale=refs[i][1], label=f"overflow {path}")
+            assert out["ws_after"]
+            nc, per_group, _ = candidate_profile(out["scores"][:60000], B)
+            if B > 3000:
+                assert nc > 4096 and per_group > 128, (nc, per_group)
+
+
 def test_very_long_unit():
     """One unit of 1.1 M rows: more than 1024 candidate workgroups and 512-row granules (eight
     emit steps per wave), with small and large budgets."""
