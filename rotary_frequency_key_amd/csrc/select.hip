@@ -28,9 +28,10 @@
 //  move_kernel.
 //
 //  hist_kernel     (standalone select only) top-digit histogram, 4096 rows per workgroup.
-//  cand_kernel     256 threads per 1024 rows (or one granule, if larger): finds the threshold's
+//  cand_kernel     256 threads per chunk of 1024 rows (or one granule, if larger), or per up to
+//                  16 consecutive chunks of a unit when the grid is large: finds the threshold's
 //                  top digit b0 from the histogram, counts per granule the keys above it and
-//                  writes the workgroup's candidates, packed, to its own region.
+//                  writes each chunk's candidates, packed, to the chunk's own region.
 //  finish_kernel   one workgroup per 64 output slots: resolves digits 2 and 3 from the unit's
 //                  candidates itself, finds the granules whose kept rows land in its slots, and
 //                  writes and gathers those rows.
@@ -163,22 +164,32 @@ __device__ __forceinline__ void load_cand_tile(const float* s, uint32_t r1, uint
   }
 }
 
-__global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a) {
+// Each workgroup takes cpw consecutive candidate workgroups' worth of rows ("chunks", 2^cand_shift
+// rows each) of one unit, finds b0 once, and writes each chunk's candidates, count and granule
+// counts as its own. Several chunks per workgroup cut the histogram reads and block scans where
+// the grid is large; one keeps the launch short where it is not. Tiles are software-pipelined:
+// the next tile's scores are loaded before the current one is counted.
+__global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a, int cpw) {
+  constexpr int kGpwMax = 1 << (kCandRowsShift - kGranMinShift);  // granules per chunk, at most
   __shared__ uint32_t sh[2 * kCW];
   __shared__ uint32_t found[2];
-  __shared__ uint32_t lgt[1 << (kCandRowsShift - kGranMinShift)];  // keys above b0 per granule
+  __shared__ uint32_t lgt[2][kGpwMax];  // keys above b0 per granule, by chunk parity
   const int WPU = a.lay.cand_wgs, gshift = a.lay.gran_shift, cshift = a.lay.cand_shift;
-  const int u = blockIdx.x / WPU, c = blockIdx.x - u * WPU;
+  const int wgpu = (WPU + cpw - 1) / cpw;  // workgroups per unit
+  const int u = blockIdx.x / wgpu, cg = blockIdx.x - u * wgpu;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const dev::UnitRows ur = dev::unit_rows(a.row_off, u, a.total_rows, a.max_rows);
   const uint32_t n = (uint32_t)ur.n;
   const uint32_t m = (uint32_t)a.B < n ? (uint32_t)a.B : n;
   if (m == n || m == 0) return;  // every row kept, or none: no threshold
-  const uint32_t r0 = (uint32_t)c << cshift;
-  if (r0 >= n) return;
-  const uint32_t r1 = n - r0 > (1u << cshift) ? r0 + (1u << cshift) : n;
+  const uint32_t nch = ((n - 1) >> cshift) + 1;  // chunks of this unit
+  const uint32_t c0 = (uint32_t)cg * (uint32_t)cpw;
+  if (c0 >= nch) return;
+  const uint32_t c1 = nch - c0 > (uint32_t)cpw ? c0 + (uint32_t)cpw : nch;
+  const uint32_t R0 = c0 << cshift, R1 = (c1 << cshift) < n ? (c1 << cshift) : n;  // this workgroup's rows
   const WsPtrs w = ws_ptrs(a);
   const float* s = a.scores + ur.beg;
+  const uint32_t gpw = 1u << (cshift - gshift);  // granules per chunk (<= kGpwMax)
 
   // loads first: 16 histogram bins per thread (4095-16t down to 4080-16t) and the first tile
   uint32_t hb[16];
@@ -191,16 +202,19 @@ __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a) {
     }
   }
   uint32_t k[kCPer];
-  load_cand_tile(s, r1, r0, k);
-  if (threadIdx.x < (1 << (kCandRowsShift - kGranMinShift))) lgt[threadIdx.x] = 0u;
+  load_cand_tile(s, R1, R0, k);
+  if (threadIdx.x < 2 * kGpwMax) lgt[threadIdx.x / kGpwMax][threadIdx.x % kGpwMax] = 0u;
 
   uint32_t above0;
-  const uint32_t b0 = block_find<kCN, 16>(hb, kHistBins, m, sh, found, &above0);
+  const uint32_t b0 = block_find<kCN, 16>(hb, kHistBins, m, sh, found, &above0);  // (synchronises)
 
+  uint32_t c = c0, par = 0;
+  uint32_t r0 = R0, r1 = R1 - R0 > (1u << cshift) ? R0 + (1u << cshift) : R1;  // the current chunk
   uint32_t* cout = w.cand + (((size_t)u * WPU + c) << cshift);
   uint32_t cbase = 0;
-  for (uint32_t t0 = r0; t0 < r1; t0 += kCTile) {
-    if (t0 != r0) load_cand_tile(s, r1, t0, k);
+  for (uint32_t t0 = R0; t0 < R1; t0 += kCTile) {
+    uint32_t kn[kCPer] = {};
+    if (t0 + kCTile < R1) load_cand_tile(s, R1, t0 + kCTile, kn);
     uint32_t ncl = 0;
 #pragma unroll
     for (int j = 0; j < kCPer; ++j) {
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a) {
       const bool in = row0 + lane < r1;
       const uint32_t d = k[j] >> kHistShift;
       const uint64_t mg = __ballot(in && d > b0);
-      if (lane == 0 && mg) atomicAdd(&lgt[(row0 - r0) >> gshift], popc64(mg));
+      if (lane == 0 && mg) atomicAdd(&lgt[par][(row0 - r0) >> gshift], popc64(mg));
       ncl += (in && d == b0) ? 1u : 0u;
     }
     uint32_t ctot;
@@ -221,17 +235,25 @@ __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a) {
       }
     }
     cbase += ctot;
+    if (t0 + kCTile >= r1) {  // the chunk is done: its granule counts and candidate count
+      __syncthreads();
+      if (threadIdx.x < gpw) {
+        const uint32_t g = (r0 >> gshift) + threadIdx.x;
+        if (g < (uint32_t)a.lay.grans) w.gran_gt[(size_t)u * a.lay.grans + g] = lgt[par][threadIdx.x];
+        lgt[par][threadIdx.x] = 0u;  // for chunk c + 2, which counts after the next chunk's barrier
+      }
+      if (threadIdx.x == 0) w.wg_cnt[(size_t)u * WPU + c] = cbase;
+      ++c;
+      par ^= 1u;
+      r0 = r1;
+      r1 = R1 - r0 > (1u << cshift) ? r0 + (1u << cshift) : R1;
+      cout += (size_t)1 << cshift;
+      cbase = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kCPer; ++j) k[j] = kn[j];
   }
-  __syncthreads();
-  const uint32_t gpw = 1u << (cshift - gshift);  // granules per workgroup (<= 16)
-  if (threadIdx.x < gpw) {
-    const uint32_t g = (r0 >> gshift) + threadIdx.x;
-    if (g < (uint32_t)a.lay.grans) w.gran_gt[(size_t)u * a.lay.grans + g] = lgt[threadIdx.x];
-  }
-  if (threadIdx.x == 0) {
-    w.wg_cnt[(size_t)u * WPU + c] = cbase;
-    if (c == 0) { w.state[u].b0 = b0; w.state[u].above0 = above0; }
-  }
+  if (threadIdx.x == 0 && c0 == 0) { w.state[u].b0 = b0; w.state[u].above0 = above0; }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1158,6 +1180,25 @@ __global__ __launch_bounds__(kTN) void topb_kernel(SelectArgs a, InplaceOut io) 
   if (t == 0) a.kept_cnt[u] = (int32_t)m;
 }
 
+// Chunks per candidate workgroup: one while the candidate grid is small, where the launch is
+// latency-bound and more workgroups finish sooner; past kCandWgTarget workgroups, chunks are
+// merged (up to 16) so that each workgroup reads the unit's histogram and scans it once for
+// several chunks.
+constexpr int64_t kCandWgTarget = 16384;
+
+int cand_chunks_per_wg(const SelectArgs& a) {
+  int cpw = 1;
+  while (cpw < 16 && (int64_t)a.n_units * ((a.lay.cand_wgs + cpw - 1) / cpw) > kCandWgTarget) cpw *= 2;
+  return cpw;
+}
+
+hipError_t launch_cand(const SelectArgs& a, int cpw, hipStream_t s) {
+  const int64_t grid = (int64_t)a.n_units * ((a.lay.cand_wgs + cpw - 1) / cpw);
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(cand_kernel, dim3((unsigned)grid), dim3(kCN), 0, s, a, cpw);
+  return hipSuccess;
+}
+
 template <bool INPLACE>
 hipError_t launch_topb(const SelectArgs& a, const InplaceOut& io, hipStream_t s) {
   const dim3 g((unsigned)a.n_units), b(kTN);
@@ -1188,11 +1229,11 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
                         a.B, a.K_out, a.V_out, a.pos_out};
     return launch_compact(c, s);
   }
-  hipLaunchKernelGGL(cand_kernel, dim3((unsigned)cand_grid), dim3(kCN), 0, s, a);
   const int64_t mm = a.B < a.max_rows ? a.B : a.max_rows;
   const int64_t fin_wgs = (int64_t)a.n_units * (mm > 0 ? (mm + kFinSlots - 1) / kFinSlots : 1);
   if (a.max_rows <= kFinishMaxRows && fin_wgs <= kFinishMaxWorkgroups) {
-    hipError_t e = hipSuccess;
+    hipError_t e = launch_cand(a, 1, s);
+    if (e != hipSuccess) return e;
     switch (a.K_out == nullptr ? 0 : a.row_bytes / 16) {
       case 0: e = launch_finish<0>(a, s); break;
       case 8: e = launch_finish<8>(a, s); break;
@@ -1203,8 +1244,9 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     return hipGetLastError();
   }
+  hipError_t e = launch_cand(a, cand_chunks_per_wg(a), s);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)U), dim3(kRN), 0, s, a);
-  hipError_t e = hipSuccess;
   if (a.K_out == nullptr) {
     e = launch_emit<0>(a, s);
   } else {
@@ -1231,7 +1273,8 @@ hipError_t launch_select_inplace(const SelectArgs& a, const MoveArgs& mv, hipStr
     e = launch_topb<true>(a, InplaceOut{mv.hole, mv.mover, (uint32_t)mv.hcap}, s);
     if (e != hipSuccess) return e;
   } else {
-    hipLaunchKernelGGL(cand_kernel, dim3((unsigned)cand_grid), dim3(kCN), 0, s, a);
+    e = launch_cand(a, cand_chunks_per_wg(a), s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(resolve_kernel, dim3((unsigned)U), dim3(kRN), 0, s, a);
     hipLaunchKernelGGL(mark_kernel, dim3((unsigned)mark_grid), dim3(kEN), 0, s, a, mv.hole, mv.mover, (uint32_t)mv.hcap);
   }
