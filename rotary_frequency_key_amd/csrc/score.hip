@@ -55,8 +55,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int c
 
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
 
-  const int unit = blockIdx.x / chunks_per_unit;
-  const int chunk = blockIdx.x - unit * chunks_per_unit;
+  const int bid = dev::xcd_block(blockIdx.x, gridDim.x);
+  const int unit = bid / chunks_per_unit;
+  const int chunk = bid - unit * chunks_per_unit;
   const dev::UnitRows ur = dev::unit_rows(a.row_off, unit, a.total_rows, a.max_rows);
   const int64_t beg = ur.beg, end = ur.beg + ur.n;
   const int64_t r0 = beg + (int64_t)chunk * RPB;

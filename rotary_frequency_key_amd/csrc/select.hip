@@ -176,7 +176,8 @@ __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a, int cpw) {
   __shared__ uint32_t lgt[2][kGpwMax];  // keys above b0 per granule, by chunk parity
   const int WPU = a.lay.cand_wgs, gshift = a.lay.gran_shift, cshift = a.lay.cand_shift;
   const int wgpu = (WPU + cpw - 1) / cpw;  // workgroups per unit
-  const int u = blockIdx.x / wgpu, cg = blockIdx.x - u * wgpu;
+  const int bid = dev::xcd_block(blockIdx.x, gridDim.x);
+  const int u = bid / wgpu, cg = bid - u * wgpu;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const dev::UnitRows ur = dev::unit_rows(a.row_off, u, a.total_rows, a.max_rows);
   const uint32_t n = (uint32_t)ur.n;
@@ -586,7 +587,8 @@ template <int CPR>  // 16-byte pieces per K/V row; 0: no gather
 __global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
   __shared__ FinShared L;
   const int NG = a.lay.grans;
-  const int u = blockIdx.x / wpu, c = blockIdx.x - u * wpu;
+  const int bid = dev::xcd_block(blockIdx.x, gridDim.x);
+  const int u = bid / wpu, c = bid - u * wpu;
   const uint32_t t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const WsPtrs w = ws_ptrs(a);

@@ -170,5 +170,19 @@ __device__ uint32_t find_bin(const H* h, int nb, uint32_t rank, uint32_t* sh, ui
   return b;
 }
 
+// Workgroup index for grids of at most kXcdRemapMaxGrid workgroups, remapped so that consecutive
+// indices run on one XCD: workgroup i is dispatched to XCD i mod 8, and index
+// (i mod 8) * (G / 8) + i / 8 (plus the remainder's share) gives each XCD one contiguous block of
+// the grid. With unit-major grids, a unit's workgroups then share an L2 in every kernel of the
+// pass, so the next kernel finds the scores, histogram and candidates it reads in that L2. Such a
+// grid runs in one wave, so no XCD gets more than its share of it. Larger grids keep launch
+// order, in which neighbouring workgroups stream neighbouring rows.
+constexpr int kXcdRemapMaxGrid = 512;
+__device__ __forceinline__ int xcd_block(int i, int G) {
+  if (G > kXcdRemapMaxGrid) return i;
+  const int x = i & 7, l = i >> 3, per = G >> 3, extra = G & 7;
+  return x * per + (x < extra ? x : extra) + l;
+}
+
 }  // namespace dev
 }  // namespace tri
