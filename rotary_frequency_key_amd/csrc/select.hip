@@ -522,9 +522,9 @@ constexpr int kFinSlots = 64;                         // output slots per workgr
 // Every finish workgroup resolves its unit's threshold again; beyond about 4096 finish
 // workgroups in all the repeated resolves cost more than the separate resolve kernel and its
 // boundary. Measured crossovers: units of 32768 rows with B = 2048 (32 finish workgroups per
-// unit): equal at 64-128 units, 2% slower at 255; units of 132096 rows with B = 12000 (188 per
-// unit): equal at 16 units, 10% slower at 32. 2048 of those units took 33.1 ms per pass with
-// finish_kernel and 17.1 ms with candidates, resolve and emit.
+// unit): equal at 160 units, 2% slower at 200; units of 65536 rows with B = 4096: 2.5% slower at
+// 96 units. 2048 units of 132096 rows with B = 12000 took 33.1 ms per pass with finish_kernel
+// and 17.1 ms with candidates, resolve and emit.
 constexpr int64_t kFinishMaxWorkgroups = 4096;
 constexpr int kFinMaxCandWgs = kFinishMaxRows >> kCandRowsShift;
 
