@@ -55,6 +55,51 @@ def test_c2_full():
         assert np.array_equal(out3[k], out[k]), k
 
 
+def test_passes_on_two_streams():
+    """Passes issued over two streams, copy c always on stream c % 2 with its own workspace and
+    outputs, as a loop compressing layer after layer may issue them: every copy ends bitwise equal
+    to the same pass run alone on one stream (no state shared between calls)."""
+    import rotary_frequency_key_amd as tri
+    from tests._parity import keys_to_device
+
+    wl = workload("c2")
+    P = pack_units(wl, [0, 1, 2], [32768, 20000, 700])
+    U, B, dev = 3, wl.budget, torch.device("cuda:0")
+    max_rows = int(np.diff(P["row_off"]).max())
+    _, mu = tri.tri_fold_weights(wl.d, wl.theta, np.array([1 << j for j in range(17)]), P["centers"][:U])
+    say("case two streams, 4 copies")
+
+    def copy_plan():
+        c = dict(K=keys_to_device(P["keys"], wl.dtype, dev), V=keys_to_device(P["values"], wl.dtype, dev),
+                 pos=torch.from_numpy(P["pos"]).to(dev), row_off=torch.from_numpy(P["row_off"]).to(dev),
+                 t=torch.from_numpy(P["t"]).to(dev), mu=torch.from_numpy(mu).to(dev))
+        outs = dict(kept_idx=torch.full((U, B), -7, dtype=torch.int32, device=dev),
+                    kept_cnt=torch.empty(U, dtype=torch.int32, device=dev),
+                    K_out=torch.zeros((U, B, wl.d), dtype=torch.bfloat16, device=dev),
+                    V_out=torch.zeros((U, B, wl.d), dtype=torch.bfloat16, device=dev),
+                    pos_out=torch.full((U, B), -5, dtype=torch.int32, device=dev))
+        plan = tri.PassPlan(c["K"], c["V"], c["pos"], c["row_off"], max_rows, c["t"], c["mu"], wl.theta, B,
+                            ws=tri.make_workspace(U, max_rows, dev),
+                            scores=torch.empty(int(P["row_off"][-1]), dtype=torch.float32, device=dev), **outs)
+        return plan, outs, c
+
+    ref_plan, ref, _ = copy_plan()
+    ref_plan.run()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    plans = []
+    for i in range(4):
+        with torch.cuda.stream(streams[i % 2]):
+            plans.append(copy_plan())
+    torch.cuda.synchronize()
+    for it in range(40):
+        plans[it % 4][0].run()
+    torch.cuda.synchronize()
+    for i, (_, outs, _) in enumerate(plans):
+        for k in ref:
+            assert torch.equal(outs[k], ref[k]), (i, k)
+
+
 def test_c3_full_size_sampled():
     """All 288 units launched; the oracle checks a sample that includes near-zero-center units;
     select self-consistency and compaction are checked on every unit."""
