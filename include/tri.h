@@ -46,7 +46,7 @@ extern "C" {
 /* status codes */
 #define TRI_OK               0
 #define TRI_ERR_ARG         -1  /* bad size, pointer, alignment or enum value */
-#define TRI_ERR_UNSUPPORTED -2  /* valid request that this build does not implement */
+#define TRI_ERR_UNSUPPORTED -2  /* valid request that the library does not implement */
 #define TRI_ERR_ALIAS       -3  /* an output range overlaps an input range or another output */
 #define TRI_ERR_WORKSPACE   -4  /* workspace missing or smaller than required */
 #define TRI_ERR_HIP         -5  /* the HIP runtime reported an error at launch */
