@@ -170,6 +170,28 @@ def test_many_units_one_workgroup_select():
             check_unit(P, i, wl, out, B, label=f"many units B={B}")
 
 
+@pytest.mark.parametrize("n_units", [130, 520])
+def test_candidate_workgroups_with_several_chunks(n_units):
+    """With max_rows above 2^18 a unit has 257 candidate chunks of 1024 rows; past 16384 chunks in
+    all, one candidate workgroup takes several consecutive chunks of its unit (4 for 130 units,
+    16 for 520). Ragged units end inside a chunk and inside a workgroup's run of chunks. The
+    results equal the bits of the one-chunk resolve path (130 units) or of the one-workgroup-per-
+    unit select (520), and sampled units match the oracle."""
+    wl = workload("c2")
+    pattern = [0, 1, 1023, 1024, 1025, 2049, 3000, 4097, 5000, 700]
+    lengths = (pattern * (n_units // len(pattern) + 1))[:n_units]
+    P = pack_units(dataclasses.replace(wl, heads=n_units), list(range(n_units)), lengths, workers=gen_workers())
+    for B in [300, 2048]:
+        say(f"case several chunks per candidate workgroup, {n_units} units, B={B}")
+        out = run_gpu(P, wl, B, max_rows=SPLIT_ROWS)
+        ref = run_gpu(P, wl, B)
+        for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
+            assert np.array_equal(out[k], ref[k]), (B, k)
+        assert out["ws_after"]
+        for i in [2, 7, 8, n_units - 2]:
+            check_unit(P, i, wl, out, B, label=f"chunks {n_units} B={B}")
+
+
 def test_all_units_empty():
     """No rows at all (zero-size inputs): every unit keeps nothing, outputs stay untouched."""
     wl = dataclasses.replace(workload("c2"), heads=3)
