@@ -28,8 +28,8 @@
 //  move_kernel.
 //
 //  hist_kernel     (standalone select only) top-digit histogram, 4096 rows per workgroup.
-//  cand_kernel     256 threads per chunk of 1024 rows (or one granule, if larger), or per up to
-//                  16 consecutive chunks of a unit when the grid is large: finds the threshold's
+//  cand_kernel     512 threads per chunk of 1024 rows (or one granule, if larger), or 256 per up
+//                  to 16 consecutive chunks of a unit when the grid is large: finds the threshold's
 //                  top digit b0 from the histogram, counts per granule the keys above it and
 //                  writes each chunk's candidates, packed, to the chunk's own region.
 //  finish_kernel   one workgroup per 64 output slots: resolves digits 2 and 3 from the unit's
@@ -148,18 +148,18 @@ __global__ __launch_bounds__(kHN) void hist_kernel(SelectArgs a, int hpu) {
 // candidates
 // ---------------------------------------------------------------------------------------------
 
-constexpr int kCN = 256;                 // threads
-constexpr int kCW = kCN / 64;            // waves
-constexpr int kCPer = 4;                 // rows per thread per tile
-constexpr int kCTile = kCN * kCPer;      // 1024 rows per tile
-static_assert(kCTile == (1 << kCandRowsShift), "tile = minimum candidate workgroup");
+// Threads per candidate workgroup: 512 (2 rows each per 1024-row tile) when a workgroup takes one
+// chunk, where the launch is latency-bound and more threads shorten the histogram scan; 256 (4
+// rows each) when it takes several, where the per-tile block scan over fewer waves costs less.
+constexpr int kCTile = 1 << kCandRowsShift;  // rows per tile
 
-// Keys of rows t0 + j*256 + threadIdx.x (j < kCPer); rows at or past r1 (> t0) read row r1 - 1.
-__device__ __forceinline__ void load_cand_tile(const float* s, uint32_t r1, uint32_t t0, uint32_t (&k)[kCPer]) {
+// Keys of rows t0 + j*NT + threadIdx.x (j < PER); rows at or past r1 (> t0) read row r1 - 1.
+template <int NT, int PER>
+__device__ __forceinline__ void load_cand_tile(const float* s, uint32_t r1, uint32_t t0, uint32_t (&k)[PER]) {
   const uint32_t last = r1 - 1;
 #pragma unroll
-  for (int j = 0; j < kCPer; ++j) {
-    const uint32_t r = t0 + j * kCN + threadIdx.x;
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t r = t0 + j * NT + threadIdx.x;
     k[j] = order_key(load_at(s, r < last ? r : last));
   }
 }
@@ -169,7 +169,11 @@ __device__ __forceinline__ void load_cand_tile(const float* s, uint32_t r1, uint
 // counts as its own. Several chunks per workgroup cut the histogram reads and block scans where
 // the grid is large; one keeps the launch short where it is not. Tiles are software-pipelined:
 // the next tile's scores are loaded before the current one is counted.
+template <int kCN>
 __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a, int cpw) {
+  constexpr int kCW = kCN / 64;           // waves
+  constexpr int kCPer = kCTile / kCN;     // rows per thread per tile
+  static_assert(kCPer * kCN == kCTile, "a tile is one chunk");
   constexpr int kGpwMax = 1 << (kCandRowsShift - kGranMinShift);  // granules per chunk, at most
   __shared__ uint32_t sh[2 * kCW];
   __shared__ uint32_t found[2];
@@ -192,22 +196,23 @@ __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a, int cpw) {
   const float* s = a.scores + ur.beg;
   const uint32_t gpw = 1u << (cshift - gshift);  // granules per chunk (<= kGpwMax)
 
-  // loads first: 16 histogram bins per thread (4095-16t down to 4080-16t) and the first tile
-  uint32_t hb[16];
+  // loads first: kBPT histogram bins per thread (4095 - kBPT*t downwards) and the first tile
+  constexpr int kBPT = kHistBins / kCN;  // histogram bins per thread
+  uint32_t hb[kBPT];
   {
     const uint4* gh4 = reinterpret_cast<const uint4*>(w.hist + (size_t)u * kHistBins);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 h = gh4[(kHistBins / 4) - 1 - 4 * threadIdx.x - q];
+    for (int q = 0; q < kBPT / 4; ++q) {
+      const uint4 h = gh4[(kHistBins / 4) - 1 - (kBPT / 4) * threadIdx.x - q];
       hb[4 * q] = h.w; hb[4 * q + 1] = h.z; hb[4 * q + 2] = h.y; hb[4 * q + 3] = h.x;
     }
   }
   uint32_t k[kCPer];
-  load_cand_tile(s, R1, R0, k);
+  load_cand_tile<kCN, kCPer>(s, R1, R0, k);
   if (threadIdx.x < 2 * kGpwMax) lgt[threadIdx.x / kGpwMax][threadIdx.x % kGpwMax] = 0u;
 
   uint32_t above0;
-  const uint32_t b0 = block_find<kCN, 16>(hb, kHistBins, m, sh, found, &above0);  // (synchronises)
+  const uint32_t b0 = block_find<kCN, kBPT>(hb, kHistBins, m, sh, found, &above0);  // (synchronises)
 
   uint32_t c = c0, par = 0;
   uint32_t r0 = R0, r1 = R1 - R0 > (1u << cshift) ? R0 + (1u << cshift) : R1;  // the current chunk
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a, int cpw) {
   uint32_t cbase = 0;
   for (uint32_t t0 = R0; t0 < R1; t0 += kCTile) {
     uint32_t kn[kCPer] = {};
-    if (t0 + kCTile < R1) load_cand_tile(s, R1, t0 + kCTile, kn);
+    if (t0 + kCTile < R1) load_cand_tile<kCN, kCPer>(s, R1, t0 + kCTile, kn);
     uint32_t ncl = 0;
 #pragma unroll
     for (int j = 0; j < kCPer; ++j) {
@@ -1197,7 +1202,8 @@ int cand_chunks_per_wg(const SelectArgs& a) {
 hipError_t launch_cand(const SelectArgs& a, int cpw, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_units * ((a.lay.cand_wgs + cpw - 1) / cpw);
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(cand_kernel, dim3((unsigned)grid), dim3(kCN), 0, s, a, cpw);
+  if (cpw == 1) hipLaunchKernelGGL(cand_kernel<512>, dim3((unsigned)grid), dim3(512), 0, s, a, cpw);
+  else hipLaunchKernelGGL(cand_kernel<256>, dim3((unsigned)grid), dim3(256), 0, s, a, cpw);
   return hipSuccess;
 }
 
