@@ -597,6 +597,31 @@ __global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
   const uint32_t t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const WsPtrs w = ws_ptrs(a);
+  // First loads, all issued before the unit's length is known (which they would otherwise wait
+  // for): the unit's state, a share of the candidates of candidate workgroup cw = t / tpw (entries
+  // ci + k*tpw), the candidate counts and the per-granule counts above the top digit, each for a
+  // unit of max_rows rows and inside the unit's regions of the workspace; what lies past the
+  // unit's own length is masked below.
+  const uint32_t mr1 = a.max_rows > 0 ? (uint32_t)(a.max_rows - 1) : 0u;  // (the regions hold one group at least)
+  const uint32_t nwg_max = (mr1 >> kCandRowsShift) + 1;  // <= kFinMaxCandWgs
+  const uint32_t ngu_max = (mr1 >> kGranMinShift) + 1;   // <= kMaxGran
+  const UnitState* st = w.state + u;
+  const uint32_t b0 = st->b0, above0 = st->above0;
+  const uint32_t* cin = w.cand + (((size_t)u * a.lay.cand_wgs) << kCandRowsShift);
+  uint32_t lg = 0;
+  while ((1u << lg) < nwg_max) ++lg;
+  const uint32_t tpw = (kRN >> lg) < kRN / 8 ? (kRN >> lg) : kRN / 8;  // threads per workgroup (>= 4)
+  const uint32_t cw = t / tpw, ci = t % tpw;
+  uint32_t pv[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) pv[k] = cw < nwg_max ? cin[((size_t)cw << kCandRowsShift) + ci + k * tpw] : 0u;
+  uint32_t wc = t < nwg_max ? w.wg_cnt[(size_t)u * a.lay.cand_wgs + t] : 0u;
+  uint32_t ggt[kRPer];
+#pragma unroll
+  for (int q = 0; q < kRPer; ++q) {
+    const uint32_t i = kRPer * t + q;
+    ggt[q] = i < ngu_max ? w.gran_gt[(size_t)u * NG + i] : 0u;
+  }
   const dev::UnitRows ur = dev::unit_rows(a.row_off, u, a.total_rows, a.max_rows);
   const uint32_t n = (uint32_t)ur.n;
   const uint32_t m = (uint32_t)a.B < n ? (uint32_t)a.B : n;
@@ -616,27 +641,14 @@ __global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
     if (t < ns) L.krow[t] = s0 + t;
     __syncthreads();
   } else {
-    const UnitState* st = w.state + u;
-    const uint32_t b0 = st->b0, above0 = st->above0;
-    const uint32_t nwg = ((n - 1) >> kCandRowsShift) + 1;  // candidate workgroups of this unit (<= 256)
-    const uint32_t ngu = ((n - 1) >> kGranMinShift) + 1;   // granules of this unit (<= 4096)
-    const uint32_t* cin = w.cand + (((size_t)u * a.lay.cand_wgs) << kCandRowsShift);
-    // loads: candidate counts, per-granule counts above the top digit, and a share of the
-    // candidates of workgroup cw = t / tpw (entries ci + k*tpw, inside the region whatever the count)
-    uint32_t lg = 0;
-    while ((1u << lg) < nwg) ++lg;
-    const uint32_t tpw = (kRN >> lg) < kRN / 8 ? (kRN >> lg) : kRN / 8;  // threads per workgroup (>= 4)
-    const uint32_t cw = t / tpw, ci = t % tpw;
+    const uint32_t nwg = ((n - 1) >> kCandRowsShift) + 1;  // candidate workgroups of this unit (<= nwg_max)
+    const uint32_t ngu = ((n - 1) >> kGranMinShift) + 1;   // granules of this unit (<= ngu_max)
     const bool pre_ok = cw < nwg;
-    uint32_t pv[kPre];
-#pragma unroll
-    for (int k = 0; k < kPre; ++k) pv[k] = pre_ok ? cin[((size_t)cw << kCandRowsShift) + ci + k * tpw] : 0u;
-    const uint32_t wc = t < nwg ? w.wg_cnt[(size_t)u * a.lay.cand_wgs + t] : 0u;
-    uint32_t ggt[kRPer];
+    if (t >= nwg) wc = 0u;
 #pragma unroll
     for (int q = 0; q < kRPer; ++q) {
       const uint32_t i = kRPer * t + q;
-      ggt[q] = i < ngu ? w.gran_gt[(size_t)u * NG + i] : 0u;
+      if (i >= ngu) ggt[q] = 0u;
       L.cnt[i] = 0u;
     }
     L.rhist[0][t] = 0u;
