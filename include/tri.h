@@ -25,7 +25,8 @@
  *    enqueued and no output is touched.
  *  - The caller owns every buffer. The library allocates no device memory and keeps no state
  *    between calls, except what a caller-provided workspace holds between the calls of one
- *    pass (the histogram from tri_score to tri_select_topb).
+ *    pass (the histogram from tri_score to tri_select_topb), and the static workspace array of
+ *    tri_prune_pass_noalloc.
  *  - Device entry points are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream). Nothing synchronises the host.
  *  - Device pointers must be 16-byte aligned unless stated otherwise.
@@ -293,6 +294,33 @@ int tri_prune_inplace(void* K, void* V, int32_t* pos, int dtype, int layout, int
                       const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
                       const int32_t* t_now, const float* mu, int B, float* scores, int32_t* kept_cnt,
                       void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * tri_prune_pass_noalloc - tri_prune_pass for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that must not call hipMalloc, harnesses that forbid it.
+ *
+ * Same arguments, checks, results and kernels as tri_prune_pass, without ws / ws_bytes: the
+ * workspace is a static device array of TRI_NOALLOC_SCRATCH_BYTES in the library's code object,
+ * one per GPU, held from the library's first launch on that GPU until the process ends. The call
+ * allocates nothing (no hipMalloc, no allocating library routine). Before the pass it zero-fills
+ * the array's histograms with a kernel of its own (one launch more than tri_prune_pass), so it
+ * does not depend on what an earlier call left in the array. Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two host threads) race, and the caller
+ * must order them.
+ *
+ *   stream  hipStream_t or NULL; a non-NULL stream must belong to the current device
+ * Errors: as tri_prune_pass; TRI_ERR_WORKSPACE, checked first, when the pass needs a workspace
+ * larger than TRI_NOALLOC_SCRATCH_BYTES (tri_prune_pass's size query gives the need: about
+ * 4 bytes per row of max_rows per unit plus 16 KB per unit, so 64 MiB holds, for example,
+ * 288 units of 32768 rows); TRI_ERR_ARG when the stream is on another device; TRI_ERR_HIP when
+ * the array's address cannot be obtained.
+ */
+#define TRI_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int tri_prune_pass_noalloc(const void* K, const void* V, int dtype, int layout, int d, double theta,
+                           const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
+                           const int32_t* pos, const int32_t* t_now, const float* mu, int B, float* scores,
+                           int32_t* kept_idx, int32_t* kept_cnt, void* K_out, void* V_out, int32_t* pos_out,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,7 @@ from ._abi import (  # noqa: F401
     TRI_DT_F32,
     TRI_KEYS_ROTATED,
     TRI_SELECT_HIST_FROM_SCORE,
+    NOALLOC_SCRATCH_BYTES,
     InplacePlan,
     MaxPassPlan,
     PassPlan,
@@ -25,6 +26,7 @@ from ._abi import (  # noqa: F401
     prune_inplace,
     prune_pass,
     prune_pass_3calls,
+    prune_pass_noalloc,
     workspace_bytes,
     score_workspace_bytes,
     tri_compact_kv,

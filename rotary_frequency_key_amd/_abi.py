@@ -17,6 +17,7 @@ TRI_BANDS_INTERLEAVED = 0
 TRI_BANDS_HALF_SPLIT = 1
 TRI_KEYS_ROTATED = 0x100  # OR into a layout: keys stored after the rotary rotation
 TRI_SELECT_HIST_FROM_SCORE = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # TRI_NOALLOC_SCRATCH_BYTES: tri_prune_pass_noalloc's static workspace
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtri.so")
@@ -48,6 +49,9 @@ def _load():
     lib.tri_prune_pass.argtypes = [vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, vp, i32,
                                    vp, vp, vp, vp, vp, vp, vp, szp, vp]
     lib.tri_prune_pass.restype = i32
+    lib.tri_prune_pass_noalloc.argtypes = [vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, vp,
+                                           i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.tri_prune_pass_noalloc.restype = i32
     lib.tri_score_max.argtypes = [vp, i32, i32, i32, ctypes.c_double, vp, i32, vp, i32, i64, i64, vp, vp, vp,
                                   vp, vp, szp, vp]
     lib.tri_score_max.restype = i32
@@ -274,7 +278,7 @@ def tri_compact_kv(K: torch.Tensor, V: torch.Tensor, pos: Optional[torch.Tensor]
 
 
 def _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, kept_idx, kept_cnt,
-               K_out, V_out, pos_out, layout):
+               K_out, V_out, pos_out, layout, with_ws=True):
     _dev(K, "K", ndim=2)
     _dev(V, "V", ndim=2)
     if V.dtype != K.dtype or V.shape != K.shape:
@@ -289,7 +293,7 @@ def _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, ke
     _dev(mu, "mu", torch.float32)
     if pos.numel() != R or t_now.numel() != U or mu.numel() != U * d:
         raise ValueError("pos, t_now or mu has the wrong size")
-    if ws is None:
+    if ws is None and with_ws:
         ws = make_workspace(U, max_rows, dev)
     if scores is None:
         scores = torch.empty(R, dtype=torch.float32, device=dev)
@@ -303,7 +307,8 @@ def _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, ke
         V_out = torch.zeros((U, B, d), dtype=K.dtype, device=dev)
     if pos_out is None:
         pos_out = torch.full((U, B), -1, dtype=torch.int32, device=dev)
-    _dev(ws, "ws", torch.uint8, 1)
+    if with_ws:
+        _dev(ws, "ws", torch.uint8, 1)
     _dev(scores, "scores", torch.float32, 1)
     _dev(kept_idx, "kept_idx", torch.int32)
     _dev(kept_cnt, "kept_cnt", torch.int32, 1)
@@ -314,12 +319,13 @@ def _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores, ke
             or K_out.numel() != U * B * d or V_out.numel() != U * B * d or pos_out.numel() != U * B):
         raise ValueError("an output has the wrong size")
     tensors = (K, V, pos, row_off, t_now, mu, ws, scores, kept_idx, kept_cnt, K_out, V_out, pos_out)
-    nbytes = ctypes.c_size_t(ws.numel())
     args = (_ptr(K), _ptr(V), dt, int(layout), int(d), float(theta), _ptr(row_off), int(U), int(R),
             int(max_rows), _ptr(pos), _ptr(t_now), _ptr(mu), int(B), _ptr(scores), _ptr(kept_idx),
-            _ptr(kept_cnt), _ptr(K_out), _ptr(V_out), _ptr(pos_out), _ptr(ws), ctypes.byref(nbytes),
-            _stream(dev))
-    return tensors, nbytes, args
+            _ptr(kept_cnt), _ptr(K_out), _ptr(V_out), _ptr(pos_out))
+    if not with_ws:
+        return tensors, None, args + (_stream(dev),)
+    nbytes = ctypes.c_size_t(ws.numel())
+    return tensors, nbytes, args + (_ptr(ws), ctypes.byref(nbytes), _stream(dev))
 
 
 def prune_pass(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=None, scores=None,
@@ -330,6 +336,18 @@ def prune_pass(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=None, sc
     tensors, nbytes, args = _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, ws, scores,
                                        kept_idx, kept_cnt, K_out, V_out, pos_out, layout)
     _check("tri_prune_pass", _lib.tri_prune_pass(*args))
+    return tensors[7], tensors[8], tensors[9], tensors[10], tensors[11], tensors[12]
+
+
+def prune_pass_noalloc(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, scores=None, kept_idx=None,
+                       kept_cnt=None, K_out=None, V_out=None, pos_out=None, layout=TRI_BANDS_INTERLEAVED):
+    """The pruning pass through tri_prune_pass_noalloc: no workspace argument, the library's static
+    device array instead (at most NOALLOC_SCRATCH_BYTES). Outputs not given are allocated here,
+    by torch, before the call; the call itself allocates nothing.
+    Returns (scores, kept_idx, kept_cnt, K_out, V_out, pos_out)."""
+    tensors, _, args = _pass_args(K, V, pos, row_off, max_rows, t_now, mu, theta, B, None, scores, kept_idx,
+                                  kept_cnt, K_out, V_out, pos_out, layout, with_ws=False)
+    _check("tri_prune_pass_noalloc", _lib.tri_prune_pass_noalloc(*args))
     return tensors[7], tensors[8], tensors[9], tensors[10], tensors[11], tensors[12]
 
 

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("score.hip", "score_max.hip", "select.hip", "compact.hip",
-                                                    "tri_api.cpp")]
+                                                    "noalloc.hip", "tri_api.cpp")]
 OUT = os.path.join(HERE, "libtri.so")
 
 HIPCC_FLAGS = [

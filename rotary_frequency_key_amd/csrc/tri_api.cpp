@@ -301,12 +301,26 @@ int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, d
                    int32_t* kept_idx, int32_t* kept_cnt, void* K_out, void* V_out, int32_t* pos_out,
                    void* ws, size_t* ws_bytes, void* stream) {
   if (n_units < 1 || max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
-  const tri::WsLayout lay = tri::ws_layout(n_units, max_rows);
-  const size_t total = lay.total;
   if (ws == nullptr && ws_bytes != nullptr) {  // size query
-    *ws_bytes = total;
+    *ws_bytes = tri::ws_layout(n_units, max_rows).total;
     return TRI_OK;
   }
+  return tri::prune_pass_run(K, V, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu,
+                             B, scores, kept_idx, kept_cnt, K_out, V_out, pos_out, ws,
+                             ws_bytes != nullptr ? *ws_bytes : 0, false, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace tri {
+
+int prune_pass_run(const void* K, const void* V, int dtype, int layout, int d, double theta, const int64_t* row_off,
+                   int n_units, int64_t total_rows, int64_t max_rows, const int32_t* pos, const int32_t* t_now,
+                   const float* mu, int B, float* scores, int32_t* kept_idx, int32_t* kept_cnt, void* K_out,
+                   void* V_out, int32_t* pos_out, void* ws, size_t ws_cap, bool clear_hist, hipStream_t s) {
+  if (n_units < 1 || max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
+  const WsLayout lay = ws_layout(n_units, max_rows);
+  const size_t total = lay.total;
   int st = check_score(K, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu, scores,
                        ws, total);
   if (st != TRI_OK) return st;
@@ -324,13 +338,13 @@ int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, d
   if (overlap(span(scores, total_rows * 4), span(kept_idx, out_rows * 4)) ||
       overlap(span(scores, total_rows * 4), span(kept_cnt, int64_t(n_units) * 4)))
     return TRI_ERR_ALIAS;
-  if (ws == nullptr || ws_bytes == nullptr || *ws_bytes < total) return TRI_ERR_WORKSPACE;
+  if (ws == nullptr || ws_cap < total) return TRI_ERR_WORKSPACE;
 
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (clear_hist && launch_clear(ws, hist_bytes(n_units), s) != hipSuccess) return TRI_ERR_HIP;
   if (launch_score_call(K, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu, scores,
                         ws, s) != hipSuccess)
     return TRI_ERR_HIP;
-  tri::SelectArgs a{};
+  SelectArgs a{};
   a.scores = scores; a.row_off = row_off; a.n_units = n_units; a.total_rows = total_rows;
   a.max_rows = max_rows; a.B = B; a.kept_idx = kept_idx; a.kept_cnt = kept_cnt;
   a.ws = ws;
@@ -340,9 +354,13 @@ int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, d
     a.K = K; a.V = V; a.pos = pos; a.row_bytes = row_bytes;
     a.K_out = K_out; a.V_out = V_out; a.pos_out = pos_out;
   }
-  if (tri::launch_select(a, s) != hipSuccess) return TRI_ERR_HIP;
+  if (launch_select(a, s) != hipSuccess) return TRI_ERR_HIP;
   return TRI_OK;
 }
+
+}  // namespace tri
+
+extern "C" {
 
 int tri_prune_inplace(void* K, void* V, int32_t* pos, int dtype, int layout, int d, double theta,
                       const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,

@@ -59,7 +59,7 @@ def run_gpu(P, wl, B, *, layout=0, centers=None, theta=None, offsets=None,
     lens = np.diff(P["row_off"])
     if max_rows is None:
         max_rows = int(lens.max()) if lens.size else 0
-    ws = tri.make_workspace(U, max_rows, dev)
+    ws = tri.make_workspace(U, max_rows, dev) if path != "noalloc" else None
     # sentinel-filled outputs: rows past kept_cnt must stay untouched
     K_out = torch.full((U, B, wl.d), 123.5, dtype=K.dtype, device=dev)
     V_out = torch.full_like(K_out, -77.0)
@@ -67,6 +67,10 @@ def run_gpu(P, wl, B, *, layout=0, centers=None, theta=None, offsets=None,
     if path == "fused":  # tri_prune_pass
         scores, kept_idx, kept_cnt, K_out, V_out, pos_out = tri.prune_pass(
             K, V, pos, row_off, max_rows, t_now, mu_d, theta, B, ws=ws, K_out=K_out, V_out=V_out,
+            pos_out=pos_out, layout=layout)
+    elif path == "noalloc":  # tri_prune_pass_noalloc: the library's static workspace, not ws
+        scores, kept_idx, kept_cnt, K_out, V_out, pos_out = tri.prune_pass_noalloc(
+            K, V, pos, row_off, max_rows, t_now, mu_d, theta, B, K_out=K_out, V_out=V_out,
             pos_out=pos_out, layout=layout)
     elif path == "calls":  # tri_score (histogram) -> tri_select_topb -> tri_compact_kv
         scores, kept_idx, kept_cnt, K_out, V_out, pos_out = tri.prune_pass_3calls(
@@ -87,7 +91,7 @@ def run_gpu(P, wl, B, *, layout=0, centers=None, theta=None, offsets=None,
         "pos_out": pos_out.cpu().numpy(),
         "mu": mu,
     }
-    out["ws_after"] = ws_at_rest(ws.cpu().numpy(), U)
+    out["ws_after"] = ws_at_rest(ws.cpu().numpy(), U) if ws is not None else None
     return out
 
 

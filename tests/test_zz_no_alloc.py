@@ -1,0 +1,81 @@
+"""tri_prune_pass_noalloc (the pass with the library's static workspace, for callers that cannot
+allocate) against tri_prune_pass with a workspace of its own: every output bit for bit, over
+consecutive calls that share the static array - the bench shape, then a smaller ragged batch,
+then the bench shape again - and its size limit and argument checks on the host."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from synthgen import pack_units, workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KEYS = ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]
+
+
+def say(*a):
+    print("[no-alloc]", *a, flush=True)
+
+
+def test_scratch_size_matches_header():
+    import rotary_frequency_key_amd as tri
+
+    hdr = open(os.path.join(ROOT, "include", "tri.h")).read()
+    m = re.search(r"#define TRI_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == tri.NOALLOC_SCRATCH_BYTES
+
+
+def test_rejects_passes_beyond_the_scratch_size():
+    """Host only: a shape whose workspace exceeds the static array returns TRI_ERR_WORKSPACE
+    before any HIP call (the fake device addresses are never used), and the limit sits where
+    tri_prune_pass's size query puts it."""
+    from rotary_frequency_key_amd import _abi
+
+    lib = _abi._lib
+    cap = _abi.NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(1 << 40)
+
+    def need(U, rows):
+        n = ctypes.c_size_t(0)
+        assert lib.tri_prune_pass(None, None, 1, 0, 128, 1e6, None, U, 0, rows, None, None, None, 2048, None,
+                                  None, None, None, None, None, None, ctypes.byref(n), None) == 0
+        return n.value
+
+    def call(U, rows):
+        return lib.tri_prune_pass_noalloc(fake, fake, 1, 0, 128, 1e6, fake, U, U * rows, rows, fake, fake, fake,
+                                          2048, fake, fake, fake, fake, fake, fake, None)
+
+    assert need(288, 32768) <= cap  # every layer of one sequence fits
+    U = 1
+    while need(U, 65536) <= cap:
+        U *= 2
+    assert call(U, 65536) == -4
+    assert call(1, 1 << 30) == -4
+    assert call(0, 1024) == -1 and call(1, -1) == -1 and call(1, 1 << 31) == -1
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_prune_pass_on_consecutive_calls():
+    import torch
+
+    from tests._parity import check_unit, gen_workers, run_gpu
+
+    wl = workload("c2")
+    P_big = pack_units(wl, workers=gen_workers())
+    P_small = pack_units(wl, [0, 1, 2, 3, 4], [0, 1, 3000, 9000, 20000])
+    cases = [("8 x 32768, B=2048", P_big, wl.budget), ("5 ragged units (0..20000 rows), B=1000", P_small, 1000),
+             ("8 x 32768, B=2048 again", P_big, wl.budget)]
+    for name, P, B in cases:
+        say(name)
+        ref = run_gpu(P, wl, B)
+        got = run_gpu(P, wl, B, path="noalloc")
+        for k in KEYS:
+            assert np.array_equal(got[k], ref[k]), (name, k)
+        assert ref["ws_after"], name
+    # the smaller call against the oracle as well
+    out = run_gpu(P_small, wl, 1000, path="noalloc")
+    for i in range(5):
+        check_unit(P_small, i, wl, out, 1000, label="no-alloc ragged")
+    torch.cuda.synchronize()
