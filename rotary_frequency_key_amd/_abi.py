@@ -20,7 +20,8 @@ TRI_SELECT_HIST_FROM_SCORE = 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # TRI_NOALLOC_SCRATCH_BYTES: tri_prune_pass_noalloc's static workspace
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libtri.so")
+# TRI_LIBRARY names another build of the same library (the host-sanitizer build of the CPU tests)
+_LIB_PATH = os.environ.get("TRI_LIBRARY") or os.path.join(_HERE, "libtri.so")
 
 
 def library_path() -> str:

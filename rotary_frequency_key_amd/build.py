@@ -39,5 +39,35 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """The library with its host code built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (the device code is unsanitized and unoptimised: this build is for the host-side tests, which
+    launch no kernel). Load it through TRI_LIBRARY with the ASan runtime preloaded
+    (asan_runtime())."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"]
+    cmd = [hipcc, *flags, "-O0", "-Xarch_host", "-g",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+           *SOURCES, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in ln]
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    return out
+
+
+def asan_runtime() -> str:
+    """Path of the ASan runtime of the compiler hipcc drives."""
+    clang = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
+    res = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("ASan runtime not found: " + (res.stdout + res.stderr))
+    return path
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
