@@ -115,6 +115,10 @@ def test_full_size_sampled(name):
         assert torch.equal(pos_out[sl][v], W["pos"][src[sl][v]])
     rng = np.random.default_rng(7)
     sample = sorted(set([0, U // 2, U - 1] + rng.choice(U, size=3, replace=False).tolist()))
+    worst, total = 0.0, 0
     for u in sample:
         err, mism = check_sample(W, wl, scores, kept_idx, B, u)
+        worst, total = max(worst, err), total + mism
         say(f"   unit {u} (N={lengths[u]}): score error {err:.3g}, kept mismatches {mism}")
+    say(f"[margin] {name.upper()} sample ({U} units, {int(lengths.min())}..{max_rows} keys, B={B}) | {worst:.3g} | "
+        f"{total} | {len(sample)}")

@@ -80,7 +80,7 @@ class Cache:
     def check_pass(self, B, label, max_rows=None):
         """Run one in-place pass and check it; then adopt the expected arrangement."""
         scores, kept_cnt, K, V, pos = self.run(B, max_rows)
-        worst = 0.0
+        worst, self.mism = 0.0, 0
         for u in range(len(self.lengths)):
             a, b = self.row_off[u], self.row_off[u + 1]
             n = b - a
@@ -91,7 +91,7 @@ class Cache:
             worst = max(worst, err)
             assert err <= TOL, (label, u, err)
             kept = O.select_topb(scores[a:b], B)  # exact on the GPU's own scores
-            kept_mismatch(kept, s_ref, scale, B)
+            self.mism += kept_mismatch(kept, s_ref, scale, B)
             src = arrangement(kept, m)
             assert np.array_equal(K[a:a + m], self.K[a:b][src]), (label, u)
             assert np.array_equal(V[a:a + m], self.V[a:b][src]), (label, u)
@@ -150,6 +150,8 @@ def test_inplace_steady_state(dtype, max_rows):
         say(f"case in-place steady state {dtype}: pass {k} (positions sparse: {np.unique(np.diff(np.sort(c.pos[:B]))).size} gaps)")
         err = c.check_pass(B, f"pass {k}", max_rows)
         say(f"   worst score error {err:.3g}")
+        say(f"[margin] in-place steady state ({dtype}, 4 units, {B} + {chunk} rows, pass {k}"
+            f"{', max_rows ' + str(max_rows) if max_rows else ''}) | {err:.3g} | {c.mism} | {U}")
 
 
 def test_inplace_rotated_keys_without_positions():

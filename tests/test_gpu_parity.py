@@ -21,6 +21,12 @@ def say(*a):
     print(*a, flush=True)
 
 
+def margin(config, err, mism, units):
+    """One line of the parity-margin record: the largest scaled score error against the oracle
+    and the keys whose kept status differs from the oracle's (each inside the tolerance band)."""
+    say(f"[margin] {config} | {err:.3g} | {mism} | {units}")
+
+
 def test_c1_full():
     wl = workload("c1")
     say("case c1: 1 x 4096 fp32 keys, B=256")
@@ -28,6 +34,7 @@ def test_c1_full():
     out = run_gpu(P, wl, wl.budget)
     err, mism = check_unit(P, 0, wl, out, wl.budget, label="c1")
     say(f"c1 score err {err:.3g}, kept mismatches in band {mism}")
+    margin("C1 (1 x 4096 fp32, B=256)", err, mism, 1)
     assert out["ws_after"]  # workspace back at rest
 
 
@@ -41,6 +48,7 @@ def test_c2_full():
         err, mism = check_unit(P, i, wl, out, wl.budget, label="c2")
         worst, total = max(worst, err), total + mism
     say(f"c2 worst score err {worst:.3g}, kept mismatches in band {total}")
+    margin("C2 (8 x 32768 bf16, B=2048)", worst, total, wl.n_units)
     assert out["ws_after"]
     # the three separate calls, the standalone select (its own histogram) and the split select
     # path (candidate, resolve, emit kernels) give the same bits
@@ -112,12 +120,12 @@ def test_c3_full_size_sampled():
     out = run_gpu(P, wl, wl.budget)
     flats = flat_units(wl)
     sample = sorted(set(flats[:3].tolist()) | {0, 143, 287})
-    worst = 0.0
+    worst, total = 0.0, 0
     for i in range(wl.n_units):
         a, b = P["row_off"][i], P["row_off"][i + 1]
         if i in sample:
             err, mism = check_unit(P, i, wl, out, wl.budget, label="c3")
-            worst = max(worst, err)
+            worst, total = max(worst, err), total + mism
             say(f"c3 unit {i} flat={i in set(flats.tolist())}: err {err:.3g} mismatches {mism}")
         else:
             kept = out["kept_idx"][i, :wl.budget]
@@ -125,6 +133,7 @@ def test_c3_full_size_sampled():
             assert np.array_equal(kept, O.select_topb(out["scores"][a:b], wl.budget)), i
             assert np.array_equal(out["K_out"][i], P["keys"][a:b][kept]), i
     say(f"c3 worst sampled score err {worst:.3g}")
+    margin("C3 sample (288 x 32768 bf16, B=2048; 3 near-zero-center units among them)", worst, total, len(sample))
 
 
 @pytest.mark.parametrize("max_rows", [None, SPLIT_ROWS])
@@ -141,6 +150,28 @@ def test_edge_cases_ragged_units(max_rows):
         for i in range(len(lengths)):
             check_unit(P, i, wl, out, B, label=f"edge B={B}")
         assert out["ws_after"]
+
+
+def test_granules_beyond_2_22_rows():
+    """max_rows above 2^22 (an upper bound only; the units are short): granules of 2^11 rows and
+    candidate chunks of two 1024-row tiles, through the pass and through the standalone select.
+    Exact against the top-B of the GPU's own scores, bit for bit equal to the same pass at the
+    natural max_rows, and the workspace back at rest."""
+    wl = workload("c2")
+    lengths = [0, 1, 5, 2049, 4100, 20000, 70000]
+    units = list(range(len(lengths)))
+    P = pack_units(dataclasses.replace(wl, heads=len(lengths)), units, lengths, workers=gen_workers())
+    big = (1 << 22) + 1
+    for B in [1, 300, 2048, 5000]:
+        say(f"case max_rows=2^22+1 B={B}")
+        ref = run_gpu(P, wl, B)
+        for path in ["fused", "standalone"]:
+            out = run_gpu(P, wl, B, max_rows=big, path=path)
+            for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
+                assert np.array_equal(out[k], ref[k]), (B, path, k)
+            assert out["ws_after"], (B, path)
+        for i in range(len(lengths)):
+            check_unit(P, i, wl, out, B, label=f"max_rows=2^22+1 B={B}")
 
 
 def test_many_units_one_workgroup_select():
@@ -368,9 +399,13 @@ def test_rotated_keys(dtype, layout):
     P, refs = _rotated_case(wl, [0, 1, 2], [5000, 1500, 33], layout)
     say(f"case rotated keys {dtype} layout {layout}")
     out = run_gpu(P, wl, 700, layout=layout | tri.TRI_KEYS_ROTATED)
+    worst, total = 0.0, 0
     for i in range(3):
         s_ref, scale = refs[i]
-        check_unit(P, i, wl, out, 700, s_ref=s_ref, scale=scale, label=f"rotated {dtype} {layout}")
+        err, mism = check_unit(P, i, wl, out, 700, s_ref=s_ref, scale=scale, label=f"rotated {dtype} {layout}")
+        worst, total = max(worst, err), total + mism
+    margin(f"rotated keys ({dtype}, {'half-split' if layout else 'interleaved'}; 5000/1500/33 rows, B=700)",
+           worst, total, 3)
     dev = torch.device("cuda:0")
     from tests._parity import keys_to_device
     alone = tri.tri_score(keys_to_device(P["keys"], dtype, dev), torch.from_numpy(P["row_off"]).to(dev),
@@ -422,6 +457,7 @@ def test_max_over_offsets(d, dtype, layout):
         kept_all, K_out = kept_idx.cpu().numpy(), keys_to_host(K_out, dtype)
         assert ws_rest(ws)
         omega = O.rotary_frequencies(d, wl.theta)
+        worst, total = 0.0, 0
         for i in range(U):
             a, b = P["row_off"][i], P["row_off"][i + 1]
             kb = O.as_bands(widen(P["keys"][a:b], dtype))
@@ -435,8 +471,10 @@ def test_max_over_offsets(d, dtype, layout):
             kept = kept_all[i, :m]
             assert np.array_equal(kept, O.select_topb(s_gpu[a:b], B))
             from tests._parity import kept_mismatch
-            kept_mismatch(kept, s_ref, scale, B)
+            worst, total = max(worst, err), total + kept_mismatch(kept, s_ref, scale, B)
             assert np.array_equal(K_out[i, :m], keys[a:b][kept])
+        margin(f"max over offsets (d={d}, {dtype}, {'half-split' if layout else 'interleaved'}, |D|={offsets.size})",
+               worst, total, U)
 
 
 def ws_rest(ws):
