@@ -507,26 +507,27 @@ def main():
         },
     }
 
-    # the same passes issued over two streams, as a serving loop that compresses layer after
-    # layer may issue them: copy c always runs on stream c % 2 (its workspace and outputs are
-    # only ever used on that stream), so one pass's select overlaps the next pass's score.
-    # Reported beside the single-stream figure, which stays the headline.
-    streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
-    oplans = []
-    for ci, c in enumerate(copies):
-        with torch.cuda.stream(streams[ci % 2]):
-            oplans.append(tri.PassPlan(c["K"], c["V"], c["pos"], c["row_off"], max_rows, c["t"], c["mu"],
-                                       wl.theta, B, ws=c["ws"], scores=c["scores"], kept_idx=c["kept_idx"],
-                                       kept_cnt=c["kept_cnt"], K_out=c["K_out"], V_out=c["V_out"],
-                                       pos_out=c["pos_out"]))
-    if len(oplans) % 2 == 0:
+    # the same passes issued over 2, 3 and 4 streams, as a serving loop that compresses layer after
+    # layer may issue them: copy c always runs on stream c % S (its workspace and outputs are only
+    # ever used on that stream), so one pass's select overlaps the next passes' scores. Reported
+    # beside the single-stream figure, which stays the headline.
+    main_stream = torch.cuda.current_stream()
+    multi = {}
+    for S in (2, 3, 4):
+        streams = [torch.cuda.Stream(device=dev) for _ in range(S)]
+        oplans = []
+        for ci, c in enumerate(copies):
+            with torch.cuda.stream(streams[ci % S]):
+                oplans.append(tri.PassPlan(c["K"], c["V"], c["pos"], c["row_off"], max_rows, c["t"], c["mu"],
+                                           wl.theta, B, ws=c["ws"], scores=c["scores"], kept_idx=c["kept_idx"],
+                                           kept_cnt=c["kept_cnt"], K_out=c["K_out"], V_out=c["V_out"],
+                                           pos_out=c["pos_out"]))
         torch.cuda.synchronize()
         for i in range(args.warmup):
             oplans[i % len(oplans)].run()
         torch.cuda.synchronize()
-        main = torch.cuda.current_stream()
         ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ea.record(main)
+        ea.record(main_stream)
         for st in streams:
             st.wait_event(ea)
         for i in range(args.steps):
@@ -534,16 +535,18 @@ def main():
         for st in streams:
             ev = torch.cuda.Event()
             ev.record(st)
-            main.wait_event(ev)
-        eb.record(main)
+            main_stream.wait_event(ev)
+        eb.record(main_stream)
         torch.cuda.synchronize()
-        ov_us = ea.elapsed_time(eb) * 1e3 / args.steps
-        result["two_streams"] = {
-            "note": "same passes, consecutive passes on two streams (independent inputs and outputs)",
-            "us_per_pass": ov_us,
-            "keys_per_s": R / (ov_us * 1e-6),
-        }
-    del oplans, streams
+        us = ea.elapsed_time(eb) * 1e3 / args.steps
+        multi[str(S)] = {"us_per_pass": us, "keys_per_s": R / (us * 1e-6),
+                         "hbm_frac_of_peak": alg_total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        del oplans, streams
+    result["multi_stream"] = {
+        "note": "the same passes, consecutive passes on S streams (copy c on stream c % S; "
+                "independent inputs, workspaces and outputs); keys are by stream count",
+        **multi,
+    }
 
     # free the pass copies before the larger caches
     del copies, plans
