@@ -554,11 +554,15 @@ def main():
     if not args.no_large:
         for name in LARGE_WORKLOADS:
             result[name] = large_workload(tri, torch, dev, args, name)
+            result[name]["frac_of_copy"] = result[name]["hbm_gbps"] / copy_gbps
             torch.cuda.empty_cache()
     if not args.no_steady:
         result["steady_state"] = steady_state(tri, torch, dev, args)
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(wl, P, B, args.cpu_seconds)
+        cb = cpu_baseline(wl, P, B, args.cpu_seconds)
+        cb["gbps"] = cb["value"] * alg_total / R / 1e9  # the same algorithmic bytes per key as the GPU's
+        cb["unfolded"]["gbps"] = cb["unfolded"]["keys_per_s"] * alg_total / R / 1e9
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 
