@@ -79,3 +79,32 @@ def test_noalloc_matches_prune_pass_on_consecutive_calls():
     for i in range(5):
         check_unit(P_small, i, wl, out, 1000, label="no-alloc ragged")
     torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+def test_noalloc_every_select_arrangement():
+    """The static workspace through the other select arrangements, each against tri_prune_pass:
+    264 ragged units (one workgroup per unit, then the compaction kernel), and ragged units and the
+    8 x 32768 layer with max_rows above 2^18 (candidates, resolve, emit); the arrangements
+    alternate, so each call starts from what a different one left in the array."""
+    import dataclasses
+
+    from tests._parity import SPLIT_ROWS, gen_workers, run_gpu
+
+    wl = workload("c2")
+    pattern = [0, 1, 5, 511, 512, 513, 2049, 4100, 20000, 300, 64]
+    lengths = pattern * 24
+    P = pack_units(dataclasses.replace(wl, heads=len(lengths)), list(range(len(lengths))), lengths,
+                   workers=gen_workers())
+    P8 = pack_units(wl, workers=gen_workers())
+    P9 = pack_units(dataclasses.replace(wl, heads=9), list(range(9)), pattern[:9])
+    # (264 units with max_rows above 2^18 would need more workspace than the static array holds)
+    for name, PP, B, mr in [("264 ragged units, B=300", P, 300, None), ("8 x 32768", P8, wl.budget, None),
+                            ("9 ragged units, max_rows 2^18+1, B=2048", P9, 2048, SPLIT_ROWS),
+                            ("8 x 32768, max_rows 2^18+1", P8, wl.budget, SPLIT_ROWS),
+                            ("264 ragged units, B=5000", P, 5000, None)]:
+        say(name)
+        ref = run_gpu(PP, wl, B, max_rows=mr)
+        got = run_gpu(PP, wl, B, max_rows=mr, path="noalloc")
+        for k in KEYS:
+            assert np.array_equal(got[k], ref[k]), (name, k)
