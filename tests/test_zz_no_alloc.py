@@ -1,7 +1,8 @@
 """tri_prune_pass_noalloc (the pass with the library's static workspace, for callers that cannot
 allocate) against tri_prune_pass with a workspace of its own: every output bit for bit, over
 consecutive calls that share the static array - the bench shape, then a smaller ragged batch,
-then the bench shape again - and its size limit and argument checks on the host."""
+then the bench shape again - through every select arrangement, captured in a HIP graph, and its
+size limit and argument checks on the host."""
 import ctypes
 import os
 import re
@@ -108,3 +109,60 @@ def test_noalloc_every_select_arrangement():
         got = run_gpu(PP, wl, B, max_rows=mr, path="noalloc")
         for k in KEYS:
             assert np.array_equal(got[k], ref[k]), (name, k)
+
+
+@pytest.mark.gpu
+def test_noalloc_pass_in_a_graph():
+    """The pass without a workspace captured in a HIP graph (torch.cuda.graph) and replayed four
+    times, with eager work and synchronisations between replays: every replay equals the eager
+    call bit for bit (the static array's address is taken by an eager call before the capture)."""
+    import torch
+
+    import rotary_frequency_key_amd as tri
+    from tests._parity import gen_workers, keys_to_device
+
+    dev = torch.device("cuda:0")
+    wl = workload("c2")
+    P = pack_units(wl, workers=gen_workers())
+    U, B = wl.n_units, wl.budget
+    max_rows = int(np.diff(P["row_off"]).max())
+    _, mu = tri.tri_fold_weights(wl.d, wl.theta, np.array([1 << j for j in range(17)]), P["centers"])
+    K, V = keys_to_device(P["keys"], "bf16", dev), keys_to_device(P["values"], "bf16", dev)
+    pos = torch.from_numpy(P["pos"]).to(dev)
+    row_off = torch.from_numpy(P["row_off"]).to(dev)
+    t_now = torch.from_numpy(P["t"]).to(dev)
+    mu_d = torch.from_numpy(mu).to(dev)
+    R = K.shape[0]
+    outs = dict(scores=torch.empty(R, dtype=torch.float32, device=dev),
+                kept_idx=torch.empty((U, B), dtype=torch.int32, device=dev),
+                kept_cnt=torch.empty(U, dtype=torch.int32, device=dev),
+                K_out=torch.empty((U, B, wl.d), dtype=torch.bfloat16, device=dev),
+                V_out=torch.empty((U, B, wl.d), dtype=torch.bfloat16, device=dev),
+                pos_out=torch.empty((U, B), dtype=torch.int32, device=dev))
+
+    def call():
+        tri.prune_pass_noalloc(K, V, pos, row_off, max_rows, t_now, mu_d, wl.theta, B, **outs)
+
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # eager, on the capture stream: the array's address is taken here, not under capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in outs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        for v in outs.values():
+            v.zero_()
+        scratch = torch.randn(1 << 20, device=dev)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in KEYS:
+            a, b = outs[k], ref[k]
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), (rep, k)
+        del scratch
