@@ -35,11 +35,12 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E spec
 # transcendentals (v_sin_f32, v_cos_f32) at half that rate.
 VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
 TRANS_LANE_OPS = VALU_LANE_OPS / 2
-# The max-over-offsets score, per key and band, needs on the vector ALU: the phase (integer
-# multiply, mask, convert, residual FMA: 4), the key-center products x and y (4), P and Q (4) and
-# their bf16 high/low split (6), plus one sine and one cosine; the offset products run on the
+# The max-over-offsets score, per key and band, needs on the vector ALU: the phase (24-bit
+# multiply, mask with the exponent, residual FMA: 3), the key's two bf16 halves as fp32 (2), the
+# key rotated by the phase (4) and the bf16 high/low split of the two products (6), plus one sine
+# and one cosine; the center and the offsets enter through the matrix product, which runs on the
 # matrix cores.
-MAX_VALU_PER_BAND, MAX_TRANS_PER_BAND = 18, 2
+MAX_VALU_PER_BAND, MAX_TRANS_PER_BAND = 15, 2
 SCORE_WARMUP = 1000  # untimed launches of the score kernel before its timed ones
 METRIC = "cached keys scored+selected/sec and achieved HBM GB/s (% of peak), 32k keys"
 

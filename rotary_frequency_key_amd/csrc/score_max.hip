@@ -187,24 +187,30 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
 // d = 128: the offset loop as a matrix product on the matrix cores
 // ---------------------------------------------------------------------------------------------
 //
-// For one row, S(delta_o) = sum_f P_f cos(w_f delta_o) - Q_f sin(w_f delta_o) is the product of
-// the row [P_0..P_63, Q_0..Q_63] with column o of W = [cos(w_f delta_o); -sin(w_f delta_o)]:
-// 16 rows x 128 x 16 offsets per v_mfma_f32_16x16x32_bf16 tile (K = 32 per instruction, four
-// steps). Each operand is split into bf16 hi + lo (x = hi + lo + O(2^-16 x)) and the product is
-// hi*hi + hi*lo + lo*hi, accumulated in fp32. A wave writes its 16 rows' P, Q (hi and lo) to an
-// LDS tile in the lane layout the instruction takes (lane L: row L % 16, k = 8 (L / 16) + i), and
-// holds W in registers for the whole workgroup. Offsets past the last repeat it (the maximum
-// does not change). The result tile gives lane L offset L % 16 of rows 4 (L / 16) + i; a DPP
-// maximum over the 16 lanes of each row group finishes the row.
+// Rotations compose by adding angles, so band f's term at offset delta_o factors into a part of
+// the key and a part of the unit:
+//     E[q_f] conj(k_f) e^{i w_f (Delta + delta_o)} = A_f W_fo,
+//     A_f = conj(k_f) e^{i w_f Delta},  W_fo = E[q_f] e^{i w_f delta_o},
+// and S(delta_o) = sum_f Re A_f Re W_fo - Im A_f Im W_fo is the product of the key's row
+// [Re A, Im A] (128 values) with column o of [Re W; -Im W]. One v_mfma_f32_16x16x32_bf16 takes
+// 16 offsets (operand A, W transposed) x 32 values of k x 16 keys (operand B); four steps cover
+// k. Each operand is split into bf16 hi + lo (x = hi + lo + O(2^-16 x)) and the product is
+// hi*hi + hi*lo + lo*hi, accumulated in fp32.
+// Operand B is computed where it is used: lane L holds key L % 16 and, at step s, the k values
+// 8 (L / 16) + i. The sum over k does not depend on the order of k, which is chosen so that these
+// are the lane's bands 16 h + 4 (L / 16) + j, four contiguous pieces of its key row: value i of
+// step s is band n = 8 (s & 1) + i of that list (n = 4 h + j), its real part for s < 2 and its
+// imaginary part for s >= 2. W's columns use the same order; the waves of a workgroup build W once
+// in LDS and each keeps it in registers. Offsets past the last repeat it (the maximum does not
+// change). The result gives lane L key L % 16 at offsets 16 t + 4 (L / 16) + i of tile t: the
+// maximum over those, then over the key's four lanes (two lane swaps), finishes the key.
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4m __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaRowsPerBlock = 512;
-constexpr int kTileStride = 136;  // bf16 per LDS tile row: 128 + 8 (16 bytes of padding against bank conflicts)
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2m __attribute__((ext_vector_type(2)));
 
 // x = hi + lo with hi, lo bf16 (round to nearest even both times)
@@ -222,18 +228,16 @@ __device__ __forceinline__ void split_bf16x2(float x0, float x1, bf16x2& hi, bf1
 template <int DT, int LAYOUT, bool HIST, int NT>  // NT: tiles of 16 offsets
 __global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a, int chunks_per_unit, BandConst bc,
                                                                      OffsetSet os) {
-  constexpr int D = 128, F = 64, LPR = 16, GPW = 4, M = 4;
-  constexpr int ROWS_WAVE = GPW * M;  // 16: one matrix tile of rows
+  constexpr int D = 128, F = 64;
   constexpr int WAVES = kMaxThreads / 64;
-  constexpr int ROWS_ITER = ROWS_WAVE * WAVES;
+  constexpr int ROWS_ITER = 16 * WAVES;  // a wave takes one tile of 16 rows per iteration
   constexpr int RPB = kMfmaRowsPerBlock;
   constexpr int ITERS = RPB / ROWS_ITER;
   static_assert(RPB % ROWS_ITER == 0, "rows per block");
   using L = RowLoad<DT, LAYOUT, D>;
   using KT = typename L::T;
 
-  __shared__ __align__(16) float2 tab[kMaxOffsets][F];                  // (cos, sin)(omega_f delta)
-  __shared__ __align__(16) __bf16 tile[WAVES][2][ROWS_WAVE][kTileStride];  // per wave: hi, lo
+  __shared__ __align__(16) bf16x8 wsh[NT][4][2][64];  // W for each lane: [tile][step][hi, lo][lane]
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
 
   const int unit = blockIdx.x / chunks_per_unit;
@@ -246,154 +250,175 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int l = lane % LPR;   // setup layout: bands 4l .. 4l+3 of rows m*GPW + gw
-  const int gw = lane / LPR;
-  const int mc = lane & 15;   // matrix layout: row (A) or offset column (B, result) ...
-  const int mq = lane >> 4;   // ... and k block 8*mq .. 8*mq+7
+  const int mc = lane & 15;  // key row of the wave's tile; offset of an offset tile
+  const int mq = lane >> 4;  // bands 16 h + 4 mq + j (h, j < 4): element n = 4 h + j of this lane
   const int n_off = os.n;
 
   const char* kbase = static_cast<const char*>(a.keys) + r0 * L::kRowBytes;
   const int32_t* pbase = a.pos + r0;
   const uint32_t last = (uint32_t)(r1 - r0 - 1);
-  const uint32_t wave_row = (uint32_t)(wave * ROWS_WAVE + gw);
-  KT kb[M];
-  int32_t pb[M];
+  const uint32_t wave_row = (uint32_t)(wave * 16 + mc);
+  KT kb[4];
+  int32_t pb;
+  {
+    const uint32_t row = min(wave_row, last);
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint32_t row = min(wave_row + m * GPW, last);
-    kb[m] = L::load(kbase, row, l);
-    pb[m] = load_pos(pbase, row);
+    for (int h = 0; h < 4; ++h) kb[h] = L::load(kbase, row, 4 * h + mq);
+    pb = load_pos(pbase, row);
   }
 
-  // the offset table, the histogram, and this lane's constants
-  for (int i = threadIdx.x; i < n_off * F; i += kMaxThreads) {
-    const int o = i / F, f = i - o * F;
-    const uint32_t dl = os.delta[o];
-    const float rev = band_phase(dl, (float)dl, bc.step[f] & 0x7FFFFFu, bc.resid[f]);
-    tab[o][f] = make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
-  }
   if constexpr (HIST) {
     for (int i = threadIdx.x; i < kHistBins; i += kMaxThreads) lhist[i] = 0u;
   }
-  uint32_t step[4];
-  float resid[4];
-  float cre[4], cim[4];
-  {
-    const float4* mp = reinterpret_cast<const float4*>(a.mu + ((size_t)unit * F + 4 * l) * 2);
-    const float4 m0 = mp[0], m1 = mp[1];
-    cre[0] = m0.x; cim[0] = m0.y; cre[1] = m0.z; cim[1] = m0.w;
-    cre[2] = m1.x; cim[2] = m1.y; cre[3] = m1.z; cim[3] = m1.w;
+  uint32_t step[16];
+  float resid[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { step[j] = bc.step[4 * l + j] & 0x7FFFFFu; resid[j] = bc.resid[4 * l + j]; }
+  for (int n = 0; n < 16; ++n) {
+    const int b = 16 * (n >> 2) + 4 * mq + (n & 3);
+    step[n] = bc.step[b] & 0x7FFFFFu;
+    resid[n] = bc.resid[b];
   }
-  CenterCoef<DT> cc;
-  cc.init(cre, cim);
   const int32_t t = a.t_now[unit];
+
+  // W = E[q_f] e^{i w_f delta_o}, operand A of the product: lane L holds offset o = 16 tt + mc
+  // (the last offset past n_off) and, at step s, k = 8 mq + i: band n = 8 (s & 1) + i of this
+  // lane, real part for s < 2, minus the imaginary part for s >= 2. Wave w builds tile w / 2,
+  // bands n = 8 (w & 1) + i (steps w & 1 and 2 + (w & 1)) for every lane, in LDS.
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {  // unrolled so that the band index is a constant
+    if (wave >= 2 * NT || (wave & 1) != hh) continue;
+    const int tt = wave >> 1;
+    const int o = min(16 * tt + mc, n_off - 1);
+    const uint32_t dlo = os.delta[o];
+    const float dfo = (float)dlo;
+    float mre[8], mim[8];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float4* mp = reinterpret_cast<const float4*>(a.mu + ((size_t)unit * F + 16 * (2 * hh + g) + 4 * mq) * 2);
+      const float4 m0 = mp[0], m1 = mp[1];
+      mre[4 * g + 0] = m0.x; mim[4 * g + 0] = m0.y; mre[4 * g + 1] = m0.z; mim[4 * g + 1] = m0.w;
+      mre[4 * g + 2] = m1.x; mim[4 * g + 2] = m1.y; mre[4 * g + 3] = m1.z; mim[4 * g + 3] = m1.w;
+    }
+    bf16x8 rh, rl, ih, il;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = 8 * hh + i;
+      const float rev = band_phase(dlo, dfo, step[n], resid[n]);
+      const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+      const float wr = fmaf(mre[i], cs, -(mim[i] * sn));
+      const float wi = fmaf(mre[i], sn, mim[i] * cs);
+      __bf16 h, lo;
+      split_bf16(wr, h, lo);
+      rh[i] = h;
+      rl[i] = lo;
+      split_bf16(-wi, h, lo);
+      ih[i] = h;
+      il[i] = lo;
+    }
+    wsh[tt][hh][0][lane] = rh;
+    wsh[tt][hh][1][lane] = rl;
+    wsh[tt][2 + hh][0][lane] = ih;
+    wsh[tt][2 + hh][1][lane] = il;
+  }
   __syncthreads();
 
-  // W in registers: tile tt, step s: column o = 16 tt + mc (the last offset past n_off), rows
-  // k = 32 s + 8 mq + i: cos(w_k delta_o) for k < 64, -sin(w_{k-64} delta_o) above
   bf16x8 whi[NT][4], wlo[NT][4];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    const int o = min(16 * tt + mc, n_off - 1);
+  for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = 32 * s + 8 * mq + i;
-        const float2 cs = tab[o][k & 63];
-        __bf16 h, lo;
-        split_bf16(k < 64 ? cs.x : -cs.y, h, lo);
-        whi[tt][s][i] = h;
-        wlo[tt][s][i] = lo;
-      }
+    for (int st = 0; st < 4; ++st) {
+      whi[tt][st] = wsh[tt][st][0][lane];
+      wlo[tt][st] = wsh[tt][st][1][lane];
     }
-  }
 
-  __bf16* th = &tile[wave][0][0][0];
-  __bf16* tl = &tile[wave][1][0][0];
+  // a row's score is stored one iteration late, halfway through the next tile, after the wait for
+  // that tile's loads: the memory counter takes loads and stores in issue order, so a wait for a
+  // load never has to wait for a store issued just before it
+  float v_prev = 0.f;
+  bool mine_prev = false;
+  uint32_t row_prev = 0;
+#pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    KT kc[M];
-    int32_t pc[M];
+    KT kc[4];
 #pragma unroll
-    for (int m = 0; m < M; ++m) { kc[m] = kb[m]; pc[m] = pb[m]; }
-    const uint32_t base = (uint32_t)(it * ROWS_ITER + wave * ROWS_WAVE);  // the wave's first row
+    for (int h = 0; h < 4; ++h) kc[h] = kb[h];
+    const int32_t pc = pb;
     if (it + 1 < ITERS) {
+      const uint32_t row = min(wave_row + (uint32_t)((it + 1) * ROWS_ITER), last);
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const uint32_t row = min(wave_row + (uint32_t)((it + 1) * ROWS_ITER) + m * GPW, last);
-        kb[m] = L::load(kbase, row, l);
-        pb[m] = load_pos(pbase, row);
-      }
+      for (int h = 0; h < 4; ++h) kb[h] = L::load(kbase, row, 4 * h + mq);
+      pb = load_pos(pbase, row);
     }
-    // per row and band: (P, Q), split, into the wave's tile (row m*GPW + gw; k = 4l + j, 64 + 4l + j)
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint32_t dl = (uint32_t)(t - pc[m]);
-      const float df = (float)dl;
-      float P[4], Q[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float rev = band_phase(dl, df, step[j], resid[j]);
-        const float sn = __builtin_amdgcn_sinf(rev);
-        const float cs = __builtin_amdgcn_cosf(rev);
-        float x, y;
-        cc.xy(kc[m], j, x, y);
-        P[j] = fmaf(x, cs, -(y * sn));
-        Q[j] = fmaf(x, sn, y * cs);
-      }
-      bf16x2 ph0, ph1, pl0, pl1, qh0, qh1, ql0, ql1;
-      split_bf16x2(P[0], P[1], ph0, pl0);
-      split_bf16x2(P[2], P[3], ph1, pl1);
-      split_bf16x2(Q[0], Q[1], qh0, ql0);
-      split_bf16x2(Q[2], Q[3], qh1, ql1);
-      const int rr = m * GPW + gw;
-      *reinterpret_cast<bf16x4*>(th + rr * kTileStride + 4 * l) = bf16x4{ph0[0], ph0[1], ph1[0], ph1[1]};
-      *reinterpret_cast<bf16x4*>(th + rr * kTileStride + 64 + 4 * l) = bf16x4{qh0[0], qh0[1], qh1[0], qh1[1]};
-      *reinterpret_cast<bf16x4*>(tl + rr * kTileStride + 4 * l) = bf16x4{pl0[0], pl0[1], pl1[0], pl1[1]};
-      *reinterpret_cast<bf16x4*>(tl + rr * kTileStride + 64 + 4 * l) = bf16x4{ql0[0], ql0[1], ql1[0], ql1[1]};
-    }
-    // the tile is this wave's own: its LDS operations run in order; keep the compiler's order too
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_sched_barrier(0);  // the next tile's loads stay in flight during this one
+    // operand B: conj(k_f) e^{i w_f Delta} of row mc, k laid out as in W
+    const uint32_t dl = (uint32_t)(t - pc);
+    const float df = (float)dl;
     f32x4m acc[NT];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4m{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(th + mc * kTileStride + 32 * s + 8 * mq);
-      const bf16x8 alo = *reinterpret_cast<const bf16x8*>(tl + mc * kTileStride + 32 * s + 8 * mq);
+    for (int hh = 0; hh < 2; ++hh) {
+      float ar[8], ai[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = 8 * hh + i;
+        const float rev = band_phase(dl, df, step[n], resid[n]);
+        const float sn = __builtin_amdgcn_sinf(rev);
+        const float cs = __builtin_amdgcn_cosf(rev);
+        float x, y;
+        if constexpr (DT == kDtBf16) {
+          const uint32_t w = kc[n >> 2].b[n & 3];
+          x = __uint_as_float(w << 16);
+          y = __uint_as_float(w & 0xFFFF0000u);
+        } else {
+          x = kc[n >> 2].re[n & 3];
+          y = kc[n >> 2].im[n & 3];
+        }
+        ar[i] = fmaf(x, cs, y * sn);
+        ai[i] = fmaf(x, sn, -(y * cs));
+      }
+      bf16x8 rhi, rlo, ihi, ilo;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        bf16x2 h2, l2;
+        split_bf16x2(ar[i], ar[i + 1], h2, l2);
+        rhi[i] = h2[0]; rhi[i + 1] = h2[1]; rlo[i] = l2[0]; rlo[i + 1] = l2[1];
+        split_bf16x2(ai[i], ai[i + 1], h2, l2);
+        ihi[i] = h2[0]; ihi[i + 1] = h2[1]; ilo[i] = l2[0]; ilo[i + 1] = l2[1];
+      }
+      if (hh == 1 && mine_prev) a.scores[r0 + row_prev] = v_prev;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, whi[tt][s], acc[tt], 0, 0, 0);
-        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, wlo[tt][s], acc[tt], 0, 0, 0);
-        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, whi[tt][s], acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[tt][hh], rhi, acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo[tt][hh], rhi, acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[tt][hh], rlo, acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[tt][2 + hh], ihi, acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo[tt][2 + hh], ihi, acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[tt][2 + hh], ilo, acc[tt], 0, 0, 0);
       }
     }
-    // the next iteration rewrites the tile only after these reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // lane L: offset column mc of rows 4 mq + i; maximum over the offsets, then over the 16 lanes
-    float best[4];
+    // lane L: row mc at offsets 16 tt + 4 mq + i; maximum over those, then over the four k blocks
+    float v = acc[0][0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = acc[0][i];
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-      for (int tt = 1; tt < NT; ++tt) v = fmaxf(v, acc[tt][i]);
-      best[i] = group_max16(v);
+      for (int i = 0; i < 4; ++i) v = fmaxf(v, acc[tt][i]);
+    {  // lanes L, L ^ 16, L ^ 32, L ^ 48 hold the same row: swap 16-lane rows, then halves
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
     }
-    if (mc < 4) {
-      const float v = mc == 0 ? best[0] : mc == 1 ? best[1] : mc == 2 ? best[2] : best[3];
-      const uint32_t row = base + 4 * mq + mc;
-      if (row <= last) {
-        a.scores[r0 + row] = v;
-        if constexpr (HIST) atomicAdd(&lhist[order_key(v) >> kHistShift], 1u);
-      }
+    const uint32_t row = (uint32_t)(it * ROWS_ITER) + wave_row;
+    const bool mine = mq == 0 && row <= last;
+    if constexpr (HIST) {
+      if (mine) atomicAdd(&lhist[order_key(v) >> kHistShift], 1u);
     }
+    v_prev = v;
+    mine_prev = mine;
+    row_prev = row;
   }
+  if (mine_prev) a.scores[r0 + row_prev] = v_prev;
 
   if constexpr (HIST) {
     __syncthreads();
