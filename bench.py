@@ -14,6 +14,8 @@ Prints ONE JSON line (rank 0). Extra legs:
   --no-cpu         skip the CPU baseline
   --no-large       skip the large device-generated workloads (all layers, ragged batch, chat pass 0)
   --no-steady      skip the chat steady state
+  --timeline       only print where one pass's time goes, from the per-workgroup stamps of the
+                   measurement build (TRI_LIBRARY=<libtri_stamps.so>, include/tri_stamps.h)
 """
 import argparse
 import hashlib
@@ -223,6 +225,7 @@ def main():
     ap.add_argument("--pmc-copy", action="store_true")
     ap.add_argument("--no-steady", action="store_true")
     ap.add_argument("--no-large", action="store_true")
+    ap.add_argument("--timeline", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -286,6 +289,10 @@ def main():
 
     def step(i):
         plans[i % len(plans)].run()
+
+    if args.timeline:
+        print(timeline(tri, torch, dev, step, args.warmup + args.steps))
+        return
 
     for i in range(args.warmup):
         step(i)
@@ -578,6 +585,52 @@ LARGE_WORKLOADS = {
     "chat_pass0": ("c5", "4 sequences x 64 layers x 8 KV heads (Qwen3-32B shape), 131072 + 1024 keys, "
                          "bf16, B=12000: candidates, resolve and emit"),
 }
+
+
+def timeline(tri, torch, dev, step, n_passes):
+    """Where one pass's time goes: the per-workgroup memory-clock stamps (100 MHz) of the last of
+    n_passes consecutive passes, read from the measurement build (libtri_stamps.so, loaded through
+    TRI_LIBRARY). Returns a markdown table."""
+    W, PNT, KN = tri.stamps_layout()
+    buf = torch.zeros(KN * W * PNT, dtype=torch.int64, device=dev)
+    tri.stamps_attach(buf)
+    for i in range(n_passes):
+        step(i)
+    torch.cuda.synchronize()
+    tri.stamps_attach(None)
+    st = buf.view(KN, W, PNT).cpu().numpy().astype(np.float64) * 0.01  # microseconds
+    def rows_with(k, pts):
+        ok = np.all(st[k][:, pts] > 0, axis=1)
+        return st[k][ok]
+    sc, ca, fi = rows_with(0, [0, 1]), rows_with(1, [0, 1]), rows_with(2, [0, 5])
+    t0 = sc[:, 0].min()
+    def span(x, a, b):
+        return x[:, a].min() - t0, x[:, b].max() - t0
+    out = [f"Last of {n_passes} consecutive passes; microseconds from the score kernel's first workgroup "
+           f"start (memory clock, 10 ns ticks). Workgroups stamped: score {len(sc)}, candidates {len(ca)}, "
+           f"finish {len(fi)}.", "", "| segment | us |", "|---|---|"]
+    s0, s1 = span(sc, 0, 1)
+    out.append(f"| `score_kernel`, first workgroup start to last end | {s0:.2f} to {s1:.2f} "
+               f"(workgroups end between {sc[:, 1].min() - t0:.2f} and {s1:.2f}, median {np.median(sc[:, 1]) - t0:.2f}) |")
+    c0, c1 = span(ca, 0, 1)
+    out.append(f"| gap to `cand_kernel`'s first workgroup | {c0 - s1:.2f} |")
+    out.append(f"| `cand_kernel` | {c1 - c0:.2f} (each workgroup {np.min(ca[:, 1] - ca[:, 0]):.2f} to "
+               f"{np.max(ca[:, 1] - ca[:, 0]):.2f}) |")
+    f0, f1 = span(fi, 0, 5)
+    out.append(f"| gap to `finish_kernel` | {f0 - c1:.2f} |")
+    out.append(f"| `finish_kernel` | {f1 - f0:.2f} (each workgroup {np.min(fi[:, 5] - fi[:, 0]):.2f} to "
+               f"{np.max(fi[:, 5] - fi[:, 0]):.2f}) |")
+    out.append(f"| pass, first score start to last finish end | {f1:.2f} |")
+    full = rows_with(2, [0, 1, 2, 3, 4, 5])
+    if len(full):
+        names = ["first loads used (state, candidates, counts)", "threshold and per-granule counts resolved",
+                 "granules listed", "granule scores re-read, kept rows placed",
+                 "indices, positions and K/V rows gathered"]
+        out += ["", f"`finish_kernel` phases, medians over its {len(full)} workgroups that run them all "
+                "(each from the workgroup's previous point):", "", "| phase | us |", "|---|---|"]
+        for j in range(1, 6):
+            out.append(f"| {names[j - 1]} | {np.median(full[:, j] - full[:, j - 1]):.2f} |")
+    return "\n".join(out)
 
 
 def large_workload(tri, torch, dev, args, name):

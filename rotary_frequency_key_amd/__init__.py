@@ -29,6 +29,8 @@ from ._abi import (  # noqa: F401
     prune_pass_noalloc,
     workspace_bytes,
     score_workspace_bytes,
+    stamps_attach,
+    stamps_layout,
     tri_compact_kv,
     tri_fold_weights,
     tri_score,

@@ -20,7 +20,8 @@ TRI_SELECT_HIST_FROM_SCORE = 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # TRI_NOALLOC_SCRATCH_BYTES: tri_prune_pass_noalloc's static workspace
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# TRI_LIBRARY names another build of the same library (the host-sanitizer build of the CPU tests)
+# TRI_LIBRARY names another build of the same library (the host-sanitizer build of the CPU tests,
+# or libtri_stamps.so, the measurement build with per-workgroup timestamps)
 _LIB_PATH = os.environ.get("TRI_LIBRARY") or os.path.join(_HERE, "libtri.so")
 
 
@@ -59,6 +60,12 @@ def _load():
     lib.tri_prune_inplace.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, i32,
                                       vp, vp, vp, szp, vp]
     lib.tri_prune_inplace.restype = i32
+    if hasattr(lib, "tri_stamps_attach"):  # the measurement build only (include/tri_stamps.h)
+        ip = ctypes.POINTER(ctypes.c_int)
+        lib.tri_stamps_layout.argtypes = [ip, ip, ip]
+        lib.tri_stamps_layout.restype = i32
+        lib.tri_stamps_attach.argtypes = [vp]
+        lib.tri_stamps_attach.restype = i32
     return lib
 
 
@@ -533,3 +540,24 @@ class PassPlan:
 
     def run(self):
         _check("tri_prune_pass", _lib.tri_prune_pass(*self._args))
+
+
+def stamps_layout():
+    """(workgroups, points, kernels) of the timestamp buffer of the measurement build
+    (include/tri_stamps.h); raises when the loaded library has no stamps."""
+    if not hasattr(_lib, "tri_stamps_layout"):
+        raise RuntimeError(f"{_LIB_PATH} has no timestamps: build libtri_stamps.so with "
+                           "`python -m rotary_frequency_key_amd.build --stamps` and load it through TRI_LIBRARY")
+    w, p, k = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check("tri_stamps_layout", _lib.tri_stamps_layout(ctypes.byref(w), ctypes.byref(p), ctypes.byref(k)))
+    return w.value, p.value, k.value
+
+
+def stamps_attach(buf: Optional[torch.Tensor]):
+    """Attach a zeroed int64 device tensor of kernels * workgroups * points entries as the
+    timestamp buffer (None detaches)."""
+    w, p, k = stamps_layout()
+    if buf is not None:
+        if buf.dtype != torch.int64 or not buf.is_cuda or buf.numel() != w * p * k or not buf.is_contiguous():
+            raise ValueError(f"the stamp buffer must be a contiguous int64 device tensor of {k * w * p} entries")
+    _check("tri_stamps_attach", _lib.tri_stamps_attach(_ptr(buf)))

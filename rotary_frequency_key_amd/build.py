@@ -1,6 +1,7 @@
 """Build libtri.so in place with hipcc for gfx950.
 
-    python -m rotary_frequency_key_amd.build      (or rotary_frequency_key_amd.build.build())
+    python -m rotary_frequency_key_amd.build           (or rotary_frequency_key_amd.build.build())
+    python -m rotary_frequency_key_amd.build --stamps  (libtri_stamps.so, the measurement build)
 """
 import os
 import subprocess
@@ -11,6 +12,7 @@ ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("score.hip", "score_max.hip", "select.hip", "compact.hip",
                                                     "noalloc.hip", "tri_api.cpp")]
 OUT = os.path.join(HERE, "libtri.so")
+STAMPS_OUT = os.path.join(HERE, "libtri_stamps.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -24,10 +26,10 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = OUT, defines=()) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = OUT + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *SOURCES, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,8 +37,14 @@ def build(verbose: bool = False) -> str:
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
+
+
+def build_stamps(out: str = STAMPS_OUT, verbose: bool = False) -> str:
+    """The library with per-workgroup memory-clock stamps in the pass's kernels (include/tri_stamps.h).
+    Load it through TRI_LIBRARY; bench.py --timeline reads the stamps of a stream of passes."""
+    return build(verbose=verbose, out=out, defines=("TRI_STAMPS",))
 
 
 def build_host_sanitized(out: str, verbose: bool = False) -> str:
@@ -70,4 +78,7 @@ def asan_runtime() -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--stamps" in sys.argv:
+        print(build_stamps(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -12,8 +12,12 @@
 //   = sum_f x_f cos(omega_f delta) - y_f sin(omega_f delta),
 //     x_f = Re(mu'_f) Re(k_f) + Im(mu'_f) Im(k_f),  y_f = Im(mu'_f) Re(k_f) - Re(mu'_f) Im(k_f).
 #include "score_device.h"
+#include "stamps.h"
 
 namespace tri {
+
+TRI_STAMPS_BUFFER(g_stamps_score)
+
 namespace {
 
 using dev::kDtBf16;
@@ -55,6 +59,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int c
 
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
 
+  TRI_STAMP(g_stamps_score, stamps::kScore, 0);
   const int bid = dev::xcd_block(blockIdx.x, gridDim.x);
   const int unit = bid / chunks_per_unit;
   const int chunk = bid - unit * chunks_per_unit;
@@ -189,6 +194,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a, int c
       if (c) atomicAdd(&gh[i], c);
     }
   }
+  TRI_STAMP(g_stamps_score, stamps::kScore, 1);
 }
 
 // Row order inside an iteration: wave w owns rows [w*ROWS_WAVE, (w+1)*ROWS_WAVE); load m of row

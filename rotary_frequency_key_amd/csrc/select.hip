@@ -48,9 +48,13 @@
 //                  (a dense run of kept rows is spread over many waves, not one CU).
 //  topb_kernel     one 1024-thread workgroup per unit, all three digits over keys held in
 //                  registers; writes the kept indices (or the in-place lists) itself.
+#include "stamps.h"
 #include "tri_device.h"
 
 namespace tri {
+
+TRI_STAMPS_BUFFER(g_stamps_select)
+
 namespace {
 
 using dev::order_key;
@@ -178,6 +182,7 @@ __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a, int cpw) {
   __shared__ uint32_t sh[2 * kCW];
   __shared__ uint32_t found[2];
   __shared__ uint32_t lgt[2][kGpwMax];  // keys above b0 per granule, by chunk parity
+  TRI_STAMP(g_stamps_select, stamps::kCand, 0);
   const int WPU = a.lay.cand_wgs, gshift = a.lay.gran_shift, cshift = a.lay.cand_shift;
   const int wgpu = (WPU + cpw - 1) / cpw;  // workgroups per unit
   const int bid = dev::xcd_block(blockIdx.x, gridDim.x);
@@ -260,6 +265,7 @@ __global__ __launch_bounds__(kCN) void cand_kernel(SelectArgs a, int cpw) {
     for (int j = 0; j < kCPer; ++j) k[j] = kn[j];
   }
   if (threadIdx.x == 0 && c0 == 0) { w.state[u].b0 = b0; w.state[u].above0 = above0; }
+  TRI_STAMP(g_stamps_select, stamps::kCand, 1);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -591,6 +597,7 @@ struct PieceCopy {
 template <int CPR>  // 16-byte pieces per K/V row; 0: no gather
 __global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
   __shared__ FinShared L;
+  TRI_STAMP(g_stamps_select, stamps::kFinish, stamps::kFinStart);
   const int NG = a.lay.grans;
   const int bid = dev::xcd_block(blockIdx.x, gridDim.x);
   const int u = bid / wpu, c = bid - u * wpu;
@@ -659,6 +666,7 @@ __global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
     if (t < nwg) L.wgoff[t] = wex;
     if (t == 0) L.wgoff[nwg] = nc;
     __syncthreads();
+    TRI_STAMP(g_stamps_select, stamps::kFinish, stamps::kFinLoads);
 
     uint32_t r = m - above0, above, T, need;
     if (nc <= (uint32_t)kCandCap) {
@@ -732,6 +740,7 @@ __global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
       });
     }
     __syncthreads();
+    TRI_STAMP(g_stamps_select, stamps::kFinish, stamps::kFinResolved);
 
     // ---- each granule's first slot; list the granules with kept rows in [s0, s0 + ns)
     uint32_t kgt[kRPer], keq[kRPer], sg = 0, se = 0;
@@ -762,6 +771,7 @@ __global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
       E = E1;
     }
     __syncthreads();
+    TRI_STAMP(g_stamps_select, stamps::kFinish, stamps::kFinListed);
 
     // ---- the listed granules' rows, one wave per granule: every kept row to its slot
     const uint32_t nsel = L.nsel < (uint32_t)kFinSlots ? L.nsel : (uint32_t)kFinSlots;
@@ -785,6 +795,7 @@ __global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
       if (keep && slot >= s0 && slot < s0 + ns) L.krow[slot - s0] = row;
     }
     __syncthreads();
+    TRI_STAMP(g_stamps_select, stamps::kFinish, stamps::kFinPlaced);
   }
 
   // ---- this workgroup's slots: indices, positions, K/V rows
@@ -801,6 +812,7 @@ __global__ __launch_bounds__(kRN) void finish_kernel(SelectArgs a, int wpu) {
     if (a.pos_out && t < ns) a.pos_out[obase + t] = pos_v;
   }
   if (t < ns) out[s0 + t] = (int32_t)my_row;
+  TRI_STAMP(g_stamps_select, stamps::kFinish, stamps::kFinEnd);
 }
 
 template <int CPR>

@@ -410,3 +410,25 @@ int tri_prune_inplace(void* K, void* V, int32_t* pos, int dtype, int layout, int
 }
 
 }  // extern "C"
+
+#ifdef TRI_STAMPS
+#include "stamps.h"
+#include "tri_stamps.h"
+
+extern "C" {
+
+int tri_stamps_layout(int* wgs, int* points, int* kernels) {
+  if (wgs) *wgs = tri::stamps::kWgs;
+  if (points) *points = tri::stamps::kPoints;
+  if (kernels) *kernels = tri::stamps::kKernels;
+  return TRI_OK;
+}
+
+int tri_stamps_attach(void* buf) {
+  if (tri::attach_g_stamps_score(buf) != hipSuccess) return TRI_ERR_HIP;
+  if (tri::attach_g_stamps_select(buf) != hipSuccess) return TRI_ERR_HIP;
+  return TRI_OK;
+}
+
+}  // extern "C"
+#endif

@@ -196,4 +196,10 @@ int prune_pass_run(const void* K, const void* V, int dtype, int layout, int d, d
 // beyond them (a.K_out etc. unused).
 hipError_t launch_select_inplace(const SelectArgs& a, const MoveArgs& mv, hipStream_t s);
 
+#ifdef TRI_STAMPS
+// The timestamp buffer pointer of each stamping source file (the measurement build only).
+hipError_t attach_g_stamps_score(void* p);
+hipError_t attach_g_stamps_select(void* p);
+#endif
+
 }  // namespace tri
