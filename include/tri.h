@@ -159,7 +159,8 @@ int tri_score(const void* keys, int dtype, int layout, int d, double theta,
  * linear and does not cover the variant that takes the maximum over them, so every offset is
  * evaluated. The rotation by the offset is applied to the key's rotated product (rotations
  * compose by adding angles, [N] "The same score, read as arrows in the plane"), so each offset
- * costs two FMAs per band.
+ * costs two FMAs per band; for d = 128 the offsets are one matrix product per 16 keys, on the
+ * matrix cores (bf16 operands split into two terms each, fp32 accumulation).
  *
  * Arguments as in tri_score, except:
  *   offsets     host int64[n_offsets], the schedule D; 0 <= delta < 2^24 each
@@ -167,7 +168,8 @@ int tri_score(const void* keys, int dtype, int layout, int d, double theta,
  *   centers     device float[n_units][F][2]: E[q_f] itself (not folded)
  *   layout      TRI_BANDS_INTERLEAVED or TRI_BANDS_HALF_SPLIT (TRI_KEYS_ROTATED: unsupported)
  * The workspace protocol is tri_score's: with ws, the histogram of these scores is added for
- * tri_select_topb (TRI_SELECT_HIST_FROM_SCORE), and tri_compact_kv completes the pass.
+ * tri_select_topb (TRI_SELECT_HIST_FROM_SCORE), and tri_compact_kv completes the pass (or
+ * tri_prune_pass_max, all three in one call).
  * Device preconditions: 0 <= t_u - pos[r] < 2^24; finite keys and centers.
  */
 int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, const int64_t* offsets,
@@ -262,6 +264,23 @@ int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, d
                    const int32_t* pos, const int32_t* t_now, const float* mu, int B, float* scores,
                    int32_t* kept_idx, int32_t* kept_cnt, void* K_out, void* V_out, int32_t* pos_out,
                    void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * tri_prune_pass_max - the pruning pass with the maximum over the offsets as the score
+ * ([N] "What it saves, and what it does not": the variant the fold does not cover): tri_score_max,
+ * tri_select_topb on its histogram and tri_compact_kv fused, same results as calling the three in
+ * turn, and the same launches as tri_prune_pass with the max-over-offsets score kernel first.
+ *
+ * Arguments as in tri_prune_pass, except offsets / n_offsets / centers / layout, which are those
+ * of tri_score_max (centers: E[q_f] itself; TRI_KEYS_ROTATED: TRI_ERR_UNSUPPORTED). The workspace
+ * is tri_prune_pass's (same size query, same rest state). Every check runs before the first
+ * launch.
+ */
+int tri_prune_pass_max(const void* K, const void* V, int dtype, int layout, int d, double theta,
+                       const int64_t* offsets, int n_offsets, const int64_t* row_off, int n_units,
+                       int64_t total_rows, int64_t max_rows, const int32_t* pos, const int32_t* t_now,
+                       const float* centers, int B, float* scores, int32_t* kept_idx, int32_t* kept_cnt,
+                       void* K_out, void* V_out, int32_t* pos_out, void* ws, size_t* ws_bytes, void* stream);
 
 /*
  * tri_prune_inplace - the pruning pass on a cache that is pruned where it lives: the steady

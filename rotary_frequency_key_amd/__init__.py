@@ -26,6 +26,7 @@ from ._abi import (  # noqa: F401
     prune_inplace,
     prune_pass,
     prune_pass_3calls,
+    prune_pass_max,
     prune_pass_noalloc,
     workspace_bytes,
     score_workspace_bytes,

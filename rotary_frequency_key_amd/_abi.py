@@ -57,6 +57,9 @@ def _load():
     lib.tri_score_max.argtypes = [vp, i32, i32, i32, ctypes.c_double, vp, i32, vp, i32, i64, i64, vp, vp, vp,
                                   vp, vp, szp, vp]
     lib.tri_score_max.restype = i32
+    lib.tri_prune_pass_max.argtypes = [vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, vp, i32, i64, i64, vp, vp,
+                                       vp, i32, vp, vp, vp, vp, vp, vp, vp, szp, vp]
+    lib.tri_prune_pass_max.restype = i32
     lib.tri_prune_inplace.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_double, vp, i32, i64, i64, vp, vp, i32,
                                       vp, vp, vp, szp, vp]
     lib.tri_prune_inplace.restype = i32
@@ -347,6 +350,19 @@ def prune_pass(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, ws=None, sc
     return tensors[7], tensors[8], tensors[9], tensors[10], tensors[11], tensors[12]
 
 
+def prune_pass_max(K, V, pos, row_off, max_rows, t_now, centers, theta, offsets, B, *, ws=None, scores=None,
+                   kept_idx=None, kept_cnt=None, K_out=None, V_out=None, pos_out=None,
+                   layout=TRI_BANDS_INTERLEAVED):
+    """One pruning pass with the maximum over the offsets as the score, through tri_prune_pass_max
+    (centers: E[q] itself). Returns (scores, kept_idx, kept_cnt, K_out, V_out, pos_out)."""
+    tensors, nbytes, args = _pass_args(K, V, pos, row_off, max_rows, t_now, centers, theta, B, ws, scores,
+                                       kept_idx, kept_cnt, K_out, V_out, pos_out, layout)
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    args = args[:6] + (offs.ctypes.data_as(ctypes.c_void_p), int(offs.size)) + args[6:]
+    _check("tri_prune_pass_max", _lib.tri_prune_pass_max(*args))
+    return tensors[7], tensors[8], tensors[9], tensors[10], tensors[11], tensors[12]
+
+
 def prune_pass_noalloc(K, V, pos, row_off, max_rows, t_now, mu, theta, B, *, scores=None, kept_idx=None,
                        kept_cnt=None, K_out=None, V_out=None, pos_out=None, layout=TRI_BANDS_INTERLEAVED):
     """The pruning pass through tri_prune_pass_noalloc: no workspace argument, the library's static
@@ -449,8 +465,9 @@ class InplacePlan:
 
 
 class MaxPassPlan:
-    """The max-over-offsets pass as three calls with arguments marshalled once: tri_score_max
-    (histogram into ws), tri_select_topb on that histogram, tri_compact_kv."""
+    """The max-over-offsets pass with arguments marshalled once: run() is tri_prune_pass_max (ws
+    sized as for tri_prune_pass), run3() the same pass as three calls (tri_score_max with its
+    histogram into ws, tri_select_topb on that histogram, tri_compact_kv), score() the score alone."""
 
     def __init__(self, K, V, pos, row_off, max_rows, t_now, centers, theta, offsets, B, *, ws, scores,
                  kept_idx, kept_cnt, K_out, V_out, pos_out, layout=TRI_BANDS_INTERLEAVED):
@@ -483,11 +500,18 @@ class MaxPassPlan:
                         _ptr(kept_cnt), _ptr(ws), nb, TRI_SELECT_HIST_FROM_SCORE, st)
         self._compact = (_ptr(K), _ptr(V), _ptr(pos), dt, int(d), _ptr(row_off), int(U), int(R), _ptr(kept_idx),
                          _ptr(kept_cnt), int(B), _ptr(K_out), _ptr(V_out), _ptr(pos_out), st)
+        self._fused = (_ptr(K), _ptr(V), dt, int(layout), int(d), float(theta),
+                       self._offs.ctypes.data_as(ctypes.c_void_p), int(self._offs.size), _ptr(row_off), int(U),
+                       int(R), int(max_rows), _ptr(pos), _ptr(t_now), _ptr(centers), int(B), _ptr(scores),
+                       _ptr(kept_idx), _ptr(kept_cnt), _ptr(K_out), _ptr(V_out), _ptr(pos_out), _ptr(ws), nb, st)
 
     def score(self):
         _check("tri_score_max", _lib.tri_score_max(*self._score))
 
     def run(self):
+        _check("tri_prune_pass_max", _lib.tri_prune_pass_max(*self._fused))
+
+    def run3(self):
         _check("tri_score_max", _lib.tri_score_max(*self._score))
         _check("tri_select_topb", _lib.tri_select_topb(*self._select))
         _check("tri_compact_kv", _lib.tri_compact_kv(*self._compact))

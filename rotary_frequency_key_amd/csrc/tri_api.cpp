@@ -130,6 +130,19 @@ int check_compact(const void* K, const void* V, const int32_t* pos, int dtype, i
   return TRI_OK;
 }
 
+// The offset set of the max-over-offsets score: 1 .. kMaxOffsets distances in [0, 2^24).
+int parse_offsets(const int64_t* offsets, int n_offsets, tri::OffsetSet* os) {
+  if (offsets == nullptr || n_offsets < 1) return TRI_ERR_ARG;
+  if (n_offsets > tri::kMaxOffsets) return TRI_ERR_UNSUPPORTED;
+  *os = tri::OffsetSet{};
+  os->n = n_offsets;
+  for (int i = 0; i < n_offsets; ++i) {
+    if (offsets[i] < 0 || offsets[i] >= (int64_t(1) << 24)) return TRI_ERR_ARG;
+    os->delta[i] = static_cast<uint32_t>(offsets[i]);
+  }
+  return TRI_OK;
+}
+
 hipError_t launch_score_call(const void* keys, int dtype, int layout, int d, double theta, const int64_t* row_off,
                              int n_units, int64_t total_rows, int64_t max_rows, const int32_t* pos,
                              const int32_t* t_now, const float* mu, float* scores, void* hist, hipStream_t s) {
@@ -224,14 +237,9 @@ int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, 
     *ws_bytes = need;
     return TRI_OK;
   }
-  if (offsets == nullptr || n_offsets < 1) return TRI_ERR_ARG;
-  if (n_offsets > tri::kMaxOffsets) return TRI_ERR_UNSUPPORTED;
-  tri::OffsetSet os{};
-  os.n = n_offsets;
-  for (int i = 0; i < n_offsets; ++i) {
-    if (offsets[i] < 0 || offsets[i] >= (int64_t(1) << 24)) return TRI_ERR_ARG;
-    os.delta[i] = static_cast<uint32_t>(offsets[i]);
-  }
+  tri::OffsetSet os;
+  const int so = parse_offsets(offsets, n_offsets, &os);
+  if (so != TRI_OK) return so;
   if ((layout & TRI_KEYS_ROTATED) != 0) return TRI_ERR_UNSUPPORTED;
   void* hist = nullptr;
   if (ws_bytes != nullptr) {
@@ -310,6 +318,25 @@ int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, d
                              ws_bytes != nullptr ? *ws_bytes : 0, false, static_cast<hipStream_t>(stream));
 }
 
+int tri_prune_pass_max(const void* K, const void* V, int dtype, int layout, int d, double theta,
+                       const int64_t* offsets, int n_offsets, const int64_t* row_off, int n_units,
+                       int64_t total_rows, int64_t max_rows, const int32_t* pos, const int32_t* t_now,
+                       const float* centers, int B, float* scores, int32_t* kept_idx, int32_t* kept_cnt,
+                       void* K_out, void* V_out, int32_t* pos_out, void* ws, size_t* ws_bytes, void* stream) {
+  if (n_units < 1 || max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
+  if (ws == nullptr && ws_bytes != nullptr) {  // size query: the workspace of tri_prune_pass
+    *ws_bytes = tri::ws_layout(n_units, max_rows).total;
+    return TRI_OK;
+  }
+  tri::OffsetSet os;
+  const int so = parse_offsets(offsets, n_offsets, &os);
+  if (so != TRI_OK) return so;
+  if ((layout & TRI_KEYS_ROTATED) != 0) return TRI_ERR_UNSUPPORTED;
+  return tri::prune_pass_run(K, V, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now,
+                             centers, B, scores, kept_idx, kept_cnt, K_out, V_out, pos_out, ws,
+                             ws_bytes != nullptr ? *ws_bytes : 0, false, static_cast<hipStream_t>(stream), &os);
+}
+
 }  // extern "C"
 
 namespace tri {
@@ -317,7 +344,8 @@ namespace tri {
 int prune_pass_run(const void* K, const void* V, int dtype, int layout, int d, double theta, const int64_t* row_off,
                    int n_units, int64_t total_rows, int64_t max_rows, const int32_t* pos, const int32_t* t_now,
                    const float* mu, int B, float* scores, int32_t* kept_idx, int32_t* kept_cnt, void* K_out,
-                   void* V_out, int32_t* pos_out, void* ws, size_t ws_cap, bool clear_hist, hipStream_t s) {
+                   void* V_out, int32_t* pos_out, void* ws, size_t ws_cap, bool clear_hist, hipStream_t s,
+                   const OffsetSet* os) {
   if (n_units < 1 || max_rows < 0 || max_rows >= (int64_t(1) << 31)) return TRI_ERR_ARG;
   const WsLayout lay = ws_layout(n_units, max_rows);
   const size_t total = lay.total;
@@ -341,9 +369,16 @@ int prune_pass_run(const void* K, const void* V, int dtype, int layout, int d, d
   if (ws == nullptr || ws_cap < total) return TRI_ERR_WORKSPACE;
 
   if (clear_hist && launch_clear(ws, hist_bytes(n_units), s) != hipSuccess) return TRI_ERR_HIP;
-  if (launch_score_call(K, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu, scores,
-                        ws, s) != hipSuccess)
+  if (os != nullptr) {  // the maximum over the offsets, from the raw centers, histogram into ws
+    BandConst bc;
+    band_constants(d, theta, &bc);
+    const ScoreArgs sa{K, dtype, layout, d, false, row_off, n_units, total_rows, max_rows, pos, t_now, mu, scores,
+                       static_cast<uint32_t*>(ws)};
+    if (launch_score_max(sa, bc, *os, s) != hipSuccess) return TRI_ERR_HIP;
+  } else if (launch_score_call(K, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu,
+                               scores, ws, s) != hipSuccess) {
     return TRI_ERR_HIP;
+  }
   SelectArgs a{};
   a.scores = scores; a.row_off = row_off; a.n_units = n_units; a.total_rows = total_rows;
   a.max_rows = max_rows; a.B = B; a.kept_idx = kept_idx; a.kept_cnt = kept_cnt;

@@ -187,11 +187,13 @@ hipError_t launch_clear(void* p, size_t bytes, hipStream_t s);
 
 // tri_prune_pass after its size query: every argument check with a workspace of ws_cap bytes at
 // ws, then the launches; with clear_hist, the workspace's histograms are zero-filled first (one
-// more launch), so it need not be in its rest state.
+// more launch), so it need not be in its rest state. With os (tri_prune_pass_max), the score is
+// the maximum over those offsets and mu holds the raw centers.
 int prune_pass_run(const void* K, const void* V, int dtype, int layout, int d, double theta, const int64_t* row_off,
                    int n_units, int64_t total_rows, int64_t max_rows, const int32_t* pos, const int32_t* t_now,
                    const float* mu, int B, float* scores, int32_t* kept_idx, int32_t* kept_cnt, void* K_out,
-                   void* V_out, int32_t* pos_out, void* ws, size_t ws_cap, bool clear_hist, hipStream_t s);
+                   void* V_out, int32_t* pos_out, void* ws, size_t ws_cap, bool clear_hist, hipStream_t s,
+                   const OffsetSet* os = nullptr);
 // tri_prune_inplace after the score: threshold, then the freed slots filled with the kept rows
 // beyond them (a.K_out etc. unused).
 hipError_t launch_select_inplace(const SelectArgs& a, const MoveArgs& mv, hipStream_t s);

@@ -170,6 +170,39 @@ def test_prune_pass_argument_errors():
     assert _prune(V=A["V"] + 8) == ARG
 
 
+def _prune_max(offsets=(1, 2, 4), **kw):
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    n = ctypes.c_size_t(1 << 40)
+    args = dict(K=A["keys"], V=A["V"], dtype=1, layout=0, d=128, theta=1e6,
+                offs=offs.ctypes.data_as(ctypes.c_void_p), noffs=offs.size, row_off=A["row_off"], U=8,
+                R=262144, maxr=32768, pos=A["pos"], t=A["t"], centers=A["mu"], B=2048, scores=A["scores"],
+                kidx=A["kidx"], kcnt=A["kcnt"], Ko=A["Ko"], Vo=A["Vo"], po=A["po"], ws=A["ws"],
+                wsb=ctypes.byref(n))
+    args.update(kw)
+    return lib.tri_prune_pass_max(*args.values(), None)
+
+
+def test_prune_pass_max_argument_errors():
+    n, m = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert _prune_max(ws=None, wsb=ctypes.byref(n)) == OK
+    assert _prune(ws=None, wsb=ctypes.byref(m)) == OK and n.value == m.value  # tri_prune_pass's workspace
+    assert _prune_max(ws=None, wsb=None) == WS
+    assert _prune_max(wsb=ctypes.byref(ctypes.c_size_t(16))) == WS
+    assert _prune_max(offsets=[]) == ARG
+    assert _prune_max(offs=None) == ARG
+    assert _prune_max(offsets=[1, -1]) == ARG
+    assert _prune_max(offsets=[1 << 24]) == ARG
+    assert _prune_max(offsets=list(range(33))) == UNSUP
+    assert _prune_max(layout=0x100) == UNSUP  # rotated keys
+    assert _prune_max(dtype=3) == ARG
+    assert _prune_max(d=96) == UNSUP
+    assert _prune_max(B=-1) == ARG
+    assert _prune_max(pos=None) == ARG
+    assert _prune_max(Ko=A["keys"]) == ALIAS
+    assert _prune_max(scores=A["kidx"]) == ALIAS
+    assert _prune_max(V=A["V"] + 8) == ARG
+
+
 def _compact(**kw):
     args = dict(K=A["keys"], V=A["V"], pos=A["pos"], dtype=1, d=128, row_off=A["row_off"], U=8,
                 R=262144, kidx=A["kidx"], kcnt=A["kcnt"], B=2048, Ko=A["Ko"], Vo=A["Vo"], po=A["po"])

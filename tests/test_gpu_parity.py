@@ -419,9 +419,9 @@ def test_rotated_keys(dtype, layout):
                                              (256, "bf16", 0)])
 def test_max_over_offsets(d, dtype, layout):
     """The maximum over the offsets of the unfolded score, against the oracle's literal loop; then
-    the select and the compaction on its histogram (score_max -> select -> compact). d = 128 runs
-    on the matrix cores: 17 offsets (one full tile of 16 and one padded), 5 (one padded tile) and
-    32 (two full tiles)."""
+    the select and the compaction on its histogram (score_max -> select -> compact), and the fused
+    pass (tri_prune_pass_max), which must give the same bits. d = 128 runs on the matrix cores:
+    17 offsets (one full tile of 16 and one padded), 5 (one padded tile) and 32 (two full tiles)."""
     import rotary_frequency_key_amd as tri
 
     wl = dataclasses.replace(workload("c2"), d=d, dtype=dtype, heads=3, theta=5e5)
@@ -452,7 +452,20 @@ def test_max_over_offsets(d, dtype, layout):
         scores = tri.tri_score_max(K, row_off, 4000, pos, t, centers, wl.theta, offsets, layout=layout, ws=ws)
         kept_idx, kept_cnt = tri.tri_select_topb(scores, row_off, 4000, B, ws=ws, hist_from_score=True)
         K_out, V_out, pos_out = tri.tri_compact_kv(K, V, pos, row_off, kept_idx, kept_cnt, B)
+        wsf = tri.make_workspace(U, 4000, dev)
+        fused = tri.prune_pass_max(K, V, pos, row_off, 4000, t, centers, wl.theta, offsets, B, ws=wsf,
+                                   layout=layout)
         torch.cuda.synchronize()
+        for x, y, name in zip(fused[:3], (scores, kept_idx, kept_cnt), ("scores", "kept_idx", "kept_cnt")):
+            assert torch.equal(x, y), f"fused pass: {name}"
+        cnt = kept_cnt.cpu().numpy()
+        for x, y, name in zip(fused[3:], (K_out, V_out, pos_out), ("K_out", "V_out", "pos_out")):
+            xb, yb = x.cpu(), y.cpu()
+            if xb.dtype == torch.bfloat16:
+                xb, yb = xb.view(torch.int16), yb.view(torch.int16)
+            for i in range(U):  # the kept rows; the slots past kept_cnt are not written
+                assert torch.equal(xb[i, :cnt[i]], yb[i, :cnt[i]]), f"fused pass: {name}, unit {i}"
+        assert ws_rest(wsf)
         s_gpu = scores.cpu().numpy()
         kept_all, K_out = kept_idx.cpu().numpy(), keys_to_host(K_out, dtype)
         assert ws_rest(ws)
