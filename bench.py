@@ -477,16 +477,20 @@ def main():
     centers = torch.from_numpy(np.ascontiguousarray(P["centers"], dtype=np.float32)).to(dev)
     ws_max = tri.make_workspace(U, max_rows, dev)
 
-    def max_plan(c, ws):
+    def max_plan(c, ws, layout=tri.TRI_BANDS_INTERLEAVED):
         return tri.MaxPassPlan(c["K"], c["V"], c["pos"], c["row_off"], max_rows, c["t"], centers, wl.theta, D, B,
                                ws=ws, scores=c["scores"], kept_idx=c["kept_idx"], kept_cnt=c["kept_cnt"],
-                               K_out=c["K_out"], V_out=c["V_out"], pos_out=c["pos_out"])
+                               K_out=c["K_out"], V_out=c["V_out"], pos_out=c["pos_out"], layout=layout)
 
     mpass = [max_plan(c, c["ws"]) for c in copies]
     mscore = [max_plan(c, ws_max) for c in copies]
+    # the same keys read as stored after the rotary rotation: a matrix product of the key rows
+    rpass = [max_plan(c, c["ws"], tri.TRI_KEYS_ROTATED) for c in copies]
+    rscore = [max_plan(c, ws_max, tri.TRI_KEYS_ROTATED) for c in copies]
     max_times = []
     nsteps = max(10, args.steps // 4)
-    for call in ([p.run for p in mpass], [p.score for p in mscore], [p.run3 for p in mpass]):
+    for call in ([p.run for p in mpass], [p.score for p in mscore], [p.run3 for p in mpass],
+                 [p.run for p in rpass], [p.score for p in rscore]):
         for i in range(args.warmup):
             call[i % len(call)]()
         torch.cuda.synchronize()
@@ -497,7 +501,7 @@ def main():
         eb.record()
         torch.cuda.synchronize()
         max_times.append(ea.elapsed_time(eb) * 1e3 / nsteps)
-    del mpass, mscore, ws_max
+    del mpass, mscore, rpass, rscore, ws_max
     F = wl.d // 2
     max_peak_keys = 1.0 / (F * MAX_VALU_PER_BAND / VALU_LANE_OPS + F * MAX_TRANS_PER_BAND / TRANS_LANE_OPS)
     max_keys = R / (max_times[1] * 1e-6)
@@ -513,6 +517,14 @@ def main():
             "achieved": max_keys, "peak": max_peak_keys, "frac": max_keys / max_peak_keys,
             "per_key": f"{F} bands x ({MAX_VALU_PER_BAND} vector lane-ops at {VALU_LANE_OPS / 1e12:.1f} T/s + "
                        f"{MAX_TRANS_PER_BAND} transcendentals at {TRANS_LANE_OPS / 1e12:.1f} T/s)",
+        },
+        "rotated_keys": {
+            "note": "the same keys read as stored after the rotary rotation: no positions and no per-key "
+                    "sine or cosine, the score a bf16 matrix product of the key rows (hbm bound)",
+            "us_per_pass": max_times[3],
+            "score_kernel_us": max_times[4],
+            "score_kernel_gbps": alg["K"] / (max_times[4] * 1e-6) / 1e9,
+            "score_kernel_frac_of_peak": alg["K"] / (max_times[4] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
         },
     }
 

@@ -166,11 +166,16 @@ int tri_score(const void* keys, int dtype, int layout, int d, double theta,
  *   offsets     host int64[n_offsets], the schedule D; 0 <= delta < 2^24 each
  *   n_offsets   1 .. 32 (more: TRI_ERR_UNSUPPORTED)
  *   centers     device float[n_units][F][2]: E[q_f] itself (not folded)
- *   layout      TRI_BANDS_INTERLEAVED or TRI_BANDS_HALF_SPLIT (TRI_KEYS_ROTATED: unsupported)
+ *   layout      TRI_BANDS_INTERLEAVED or TRI_BANDS_HALF_SPLIT, optionally | TRI_KEYS_ROTATED: the keys
+ *               were stored after the rotary rotation at their positions; then
+ *               conj(k) e^{i omega (t - p + delta)} = conj(k_rot) e^{i omega (t + delta)}, pos is not
+ *               read (it may be NULL), and for d = 128 the score is a matrix product of the stored
+ *               key rows themselves (no per-key sine or cosine)
  * The workspace protocol is tri_score's: with ws, the histogram of these scores is added for
  * tri_select_topb (TRI_SELECT_HIST_FROM_SCORE), and tri_compact_kv completes the pass (or
  * tri_prune_pass_max, all three in one call).
- * Device preconditions: 0 <= t_u - pos[r] < 2^24; finite keys and centers.
+ * Device preconditions: 0 <= t_u - pos[r] < 2^24 (rotated keys: 0 <= t_u < 2^24); finite keys
+ * and centers.
  */
 int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, const int64_t* offsets,
                   int n_offsets, const int64_t* row_off, int n_units, int64_t total_rows, int64_t max_rows,
@@ -272,7 +277,8 @@ int tri_prune_pass(const void* K, const void* V, int dtype, int layout, int d, d
  * turn, and the same launches as tri_prune_pass with the max-over-offsets score kernel first.
  *
  * Arguments as in tri_prune_pass, except offsets / n_offsets / centers / layout, which are those
- * of tri_score_max (centers: E[q_f] itself; TRI_KEYS_ROTATED: TRI_ERR_UNSUPPORTED). The workspace
+ * of tri_score_max (centers: E[q_f] itself; with TRI_KEYS_ROTATED, pos may be NULL when pos_out
+ * is NULL). The workspace
  * is tri_prune_pass's (same size query, same rest state). Every check runs before the first
  * launch.
  */

@@ -194,22 +194,25 @@ def tri_score(keys: torch.Tensor, row_off: torch.Tensor, max_rows: int, pos: Opt
     return scores
 
 
-def tri_score_max(keys: torch.Tensor, row_off: torch.Tensor, max_rows: int, pos: torch.Tensor,
+def tri_score_max(keys: torch.Tensor, row_off: torch.Tensor, max_rows: int, pos: Optional[torch.Tensor],
                   t_now: torch.Tensor, centers: torch.Tensor, theta: float, offsets, *,
                   layout: int = TRI_BANDS_INTERLEAVED, scores: Optional[torch.Tensor] = None,
                   ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Maximum over the offset schedule of the unfolded score; centers are E[q] (device float32
-    [U][d/2][2]), offsets a host sequence of ints."""
+    [U][d/2][2]), offsets a host sequence of ints. pos may be None with TRI_KEYS_ROTATED."""
     _dev(keys, "keys", ndim=2)
     dt = _key_dtype(keys)
     R, d = keys.shape
     _dev(row_off, "row_off", torch.int64, 1)
     U = row_off.numel() - 1
-    _dev(pos, "pos", torch.int32, 1)
+    if pos is not None:
+        _dev(pos, "pos", torch.int32, 1)
+        if pos.numel() != R:
+            raise ValueError("pos has the wrong size")
     _dev(t_now, "t_now", torch.int32, 1)
     _dev(centers, "centers", torch.float32)
-    if pos.numel() != R or t_now.numel() != U or centers.numel() != U * d:
-        raise ValueError("pos, t_now or centers has the wrong size")
+    if t_now.numel() != U or centers.numel() != U * d:
+        raise ValueError("t_now or centers has the wrong size")
     offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
     if scores is None:
         scores = torch.empty(R, dtype=torch.float32, device=keys.device)

@@ -49,7 +49,9 @@ __device__ __forceinline__ float group_max16(float v) {
   return fmaxf(v, dpp_f<0x140>(v));  // row_mirror
 }
 
-template <int DT, int LAYOUT, int D, bool HIST>
+// ROT: keys stored after the rotary rotation at their positions; conj(k) e^{i w (t - p + delta)}
+// = conj(k_rot) e^{i w (t + delta)}, so the same evaluation with every position taken as 0.
+template <int DT, int LAYOUT, int D, bool HIST, bool ROT>
 __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int chunks_per_unit, BandConst bc,
                                                                 OffsetSet os) {
   constexpr int F = D / 2;
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
   const int n_off = os.n;
 
   const char* kbase = static_cast<const char*>(a.keys) + r0 * L::kRowBytes;
-  const int32_t* pbase = a.pos + r0;
+  const int32_t* pbase = ROT ? nullptr : a.pos + r0;
   const uint32_t last = (uint32_t)(r1 - r0 - 1);
   const uint32_t wave_row = (uint32_t)(wave * ROWS_WAVE + gw);
   KT kb[M];
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
   for (int m = 0; m < M; ++m) {
     const uint32_t row = min(wave_row + m * GPW, last);
     kb[m] = L::load(kbase, row, l);
-    pb[m] = load_pos(pbase, row);
+    pb[m] = ROT ? 0 : load_pos(pbase, row);
   }
 
   // the offset table, the histogram, and this lane's constants
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
       for (int m = 0; m < M; ++m) {
         const uint32_t row = min(base + ROWS_ITER + m * GPW, last);
         kb[m] = L::load(kbase, row, l);
-        pb[m] = load_pos(pbase, row);
+        pb[m] = ROT ? 0 : load_pos(pbase, row);
       }
     }
     // per row and band: the center term rotated by the distance, (P, Q)
@@ -430,6 +432,189 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a
   }
 }
 
+// Keys stored after the rotary rotation (k_rot = k e^{i w p}; "The same score, read as arrows in
+// the plane": rotations compose by adding angles): conj(k_f) e^{i w_f (t - p + delta)} =
+// conj(k_rot_f) e^{i w_f (t + delta)}. With P_fo = E[q_f] e^{i w_f (t + delta_o)}, one value per
+// unit, band and offset, and k_rot_f = x_f + i y_f,
+//     S(delta_o) = sum_f Re(P_fo) x_f + Im(P_fo) y_f,
+// the product of the key row itself (128 values in memory order) with W[e][o] = Re or Im of
+// P_{f(e), o}, e the element of the row and f(e) its band. There is no per-key trigonometry: bf16
+// keys are exact bf16 operands (W split into hi + lo: two products per step), fp32 keys are split
+// like W (three). Lane L holds key L % 16 and, at step s, elements 32 s + 8 (L / 16) + i of it:
+// one 16-byte piece of the row for bf16, two for fp32. W, the result and the stores are as in
+// score_max_mfma_kernel.
+template <int DT, int LAYOUT, bool HIST, int NT>  // NT: tiles of 16 offsets
+__global__ __launch_bounds__(kMaxThreads) void score_max_rot_mfma_kernel(ScoreArgs a, int chunks_per_unit,
+                                                                         BandConst bc, OffsetSet os) {
+  constexpr int D = 128, F = 64;
+  constexpr int WAVES = kMaxThreads / 64;
+  constexpr int ROWS_ITER = 16 * WAVES;
+  constexpr int RPB = kMfmaRowsPerBlock;
+  constexpr int ITERS = RPB / ROWS_ITER;
+  static_assert(RPB % ROWS_ITER == 0, "rows per block");
+  constexpr int EB = DT == kDtBf16 ? 2 : 4;  // bytes per element
+  constexpr uint32_t ROW_BYTES = D * EB;
+  constexpr int PIECES = 8 * EB / 16;        // 16-byte pieces per 8 elements
+  constexpr int PF = 3;                      // tiles of loads in flight ahead of the one in use
+  static_assert(ITERS > PF, "tiles per wave");
+
+  __shared__ __align__(16) bf16x8 wsh[NT][4][2][64];  // W for each lane: [tile][step][hi, lo][lane]
+  __shared__ uint32_t lhist[HIST ? kHistBins : 1];
+
+  const int unit = blockIdx.x / chunks_per_unit;
+  const int chunk = blockIdx.x - unit * chunks_per_unit;
+  const dev::UnitRows ur = dev::unit_rows(a.row_off, unit, a.total_rows, a.max_rows);
+  const int64_t beg = ur.beg, end = ur.beg + ur.n;
+  const int64_t r0 = beg + (int64_t)chunk * RPB;
+  if (r0 >= end) return;
+  const int64_t r1 = (end - r0 < RPB) ? end : r0 + RPB;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int mc = lane & 15;  // key row of the wave's tile; offset of an offset tile
+  const int mq = lane >> 4;  // elements 32 s + 8 mq + i of the row at step s
+  const int n_off = os.n;
+
+  const char* kbase = static_cast<const char*>(a.keys) + r0 * (int64_t)ROW_BYTES;
+  const uint32_t last = (uint32_t)(r1 - r0 - 1);
+  const uint32_t wave_row = (uint32_t)(wave * 16 + mc);
+  // a ring of PF + 1 tiles in registers (the loop is unrolled): tile it in use, it + 1 .. it + PF
+  // in flight; with one tile ahead a CU keeps too few bytes in flight to cover the memory latency
+  u32x4 kq[PF + 1][4][PIECES];
+  auto load_tile = [&](int j, int slot) {
+    const uint32_t row = min(wave_row + (uint32_t)(j * ROWS_ITER), last);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int q = 0; q < PIECES; ++q)
+        kq[slot][st][q] = ld_stream<u32x4>(kbase, row * ROW_BYTES + (uint32_t)((32 * st + 8 * mq) * EB + 16 * q));
+  };
+#pragma unroll
+  for (int j = 0; j < PF; ++j) load_tile(j, j);
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < kHistBins; i += kMaxThreads) lhist[i] = 0u;
+  }
+
+  // W, operand A: lane L holds offset o = 16 tt + mc (the last offset past n_off) and, at step s,
+  // W[32 s + 8 mq + i][o]. Wave w builds tile w / 2, steps 2 (w & 1) and 2 (w & 1) + 1, in LDS.
+  const uint32_t t = (uint32_t)a.t_now[unit];
+  if (wave < 2 * NT) {
+    const int tt = wave >> 1;
+    const int o = min(16 * tt + mc, n_off - 1);
+    const uint32_t dlo = os.delta[o];
+    const float2* mu2 = reinterpret_cast<const float2*>(a.mu) + (size_t)unit * F;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int st = 2 * (wave & 1) + s2;
+      bf16x8 h8, l8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = 32 * st + 8 * mq + i;
+        const int f = LAYOUT == kInterleaved ? e >> 1 : e & 63;
+        const bool im = LAYOUT == kInterleaved ? (e & 1) != 0 : e >= 64;
+        const uint32_t step = bc.step[f] & 0x7FFFFFu;
+        const float resid = bc.resid[f];
+        const float rt = band_phase(t, (float)t, step, resid);
+        const float rd = band_phase(dlo, (float)dlo, step, resid);
+        const float ct = __builtin_amdgcn_cosf(rt), snt = __builtin_amdgcn_sinf(rt);
+        const float cd = __builtin_amdgcn_cosf(rd), snd = __builtin_amdgcn_sinf(rd);
+        const float er = fmaf(ct, cd, -(snt * snd)), ei = fmaf(ct, snd, snt * cd);  // e^{i w (t + delta)}
+        const float2 m = mu2[f];
+        const float w = im ? fmaf(m.x, ei, m.y * er) : fmaf(m.x, er, -(m.y * ei));
+        __bf16 h, lo;
+        split_bf16(w, h, lo);
+        h8[i] = h;
+        l8[i] = lo;
+      }
+      wsh[tt][st][0][lane] = h8;
+      wsh[tt][st][1][lane] = l8;
+    }
+  }
+  __syncthreads();
+
+  bf16x8 whi[NT][4], wlo[NT][4];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      whi[tt][st] = wsh[tt][st][0][lane];
+      wlo[tt][st] = wsh[tt][st][1][lane];
+    }
+
+  // scores stored one iteration late, halfway through the next tile (as in score_max_mfma_kernel)
+  float v_prev = 0.f;
+  bool mine_prev = false;
+  uint32_t row_prev = 0;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    if (it + PF < ITERS) load_tile(it + PF, (it + PF) % (PF + 1));
+    const auto& kc = kq[it % (PF + 1)];
+    __builtin_amdgcn_sched_barrier(0);  // the next tile's loads stay in flight during this one
+    f32x4m acc[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4m{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (st == 2 && mine_prev) a.scores[r0 + row_prev] = v_prev;
+      if constexpr (DT == kDtBf16) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, kc[st][0]);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[tt][st], kv, acc[tt], 0, 0, 0);
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo[tt][st], kv, acc[tt], 0, 0, 0);
+        }
+      } else {
+        bf16x8 khi, klo;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; j += 2) {
+            bf16x2 h2, l2;
+            split_bf16x2(__uint_as_float(kc[st][q][j]), __uint_as_float(kc[st][q][j + 1]), h2, l2);
+            khi[4 * q + j] = h2[0]; khi[4 * q + j + 1] = h2[1];
+            klo[4 * q + j] = l2[0]; klo[4 * q + j + 1] = l2[1];
+          }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[tt][st], khi, acc[tt], 0, 0, 0);
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo[tt][st], khi, acc[tt], 0, 0, 0);
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi[tt][st], klo, acc[tt], 0, 0, 0);
+        }
+      }
+    }
+    // lane L: row mc at offsets 16 tt + 4 mq + i; maximum over those, then over the four k blocks
+    float v = acc[0][0];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v = fmaxf(v, acc[tt][i]);
+    {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+    }
+    const uint32_t row = (uint32_t)(it * ROWS_ITER) + wave_row;
+    const bool mine = mq == 0 && row <= last;
+    if constexpr (HIST) {
+      if (mine) atomicAdd(&lhist[order_key(v) >> kHistShift], 1u);
+    }
+    v_prev = v;
+    mine_prev = mine;
+    row_prev = row;
+  }
+  if (mine_prev) a.scores[r0 + row_prev] = v_prev;
+
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* gh = a.hist + (size_t)unit * kHistBins;
+    for (int i = threadIdx.x; i < kHistBins; i += kMaxThreads) {
+      const uint32_t c = lhist[i];
+      if (c) atomicAdd(&gh[i], c);
+    }
+  }
+}
+
 template <int DT, int LAYOUT, int NT>
 hipError_t launch_mfma(const ScoreArgs& a, const BandConst& bc, const OffsetSet& os, hipStream_t s) {
   constexpr int RPB = kMfmaRowsPerBlock;
@@ -438,8 +623,16 @@ hipError_t launch_mfma(const ScoreArgs& a, const BandConst& bc, const OffsetSet&
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid), b(kMaxThreads);
-  if (a.hist) hipLaunchKernelGGL((score_max_mfma_kernel<DT, LAYOUT, true, NT>), g, b, 0, s, a, (int)chunks, bc, os);
-  else hipLaunchKernelGGL((score_max_mfma_kernel<DT, LAYOUT, false, NT>), g, b, 0, s, a, (int)chunks, bc, os);
+  if (a.rotated) {
+    if (a.hist)
+      hipLaunchKernelGGL((score_max_rot_mfma_kernel<DT, LAYOUT, true, NT>), g, b, 0, s, a, (int)chunks, bc, os);
+    else
+      hipLaunchKernelGGL((score_max_rot_mfma_kernel<DT, LAYOUT, false, NT>), g, b, 0, s, a, (int)chunks, bc, os);
+  } else if (a.hist) {
+    hipLaunchKernelGGL((score_max_mfma_kernel<DT, LAYOUT, true, NT>), g, b, 0, s, a, (int)chunks, bc, os);
+  } else {
+    hipLaunchKernelGGL((score_max_mfma_kernel<DT, LAYOUT, false, NT>), g, b, 0, s, a, (int)chunks, bc, os);
+  }
   return hipGetLastError();
 }
 
@@ -451,8 +644,14 @@ hipError_t launch_t(const ScoreArgs& a, const BandConst& bc, const OffsetSet& os
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid), b(kMaxThreads);
-  if (a.hist) hipLaunchKernelGGL((score_max_kernel<DT, LAYOUT, D, true>), g, b, 0, s, a, (int)chunks, bc, os);
-  else hipLaunchKernelGGL((score_max_kernel<DT, LAYOUT, D, false>), g, b, 0, s, a, (int)chunks, bc, os);
+  if (a.rotated) {
+    if (a.hist) hipLaunchKernelGGL((score_max_kernel<DT, LAYOUT, D, true, true>), g, b, 0, s, a, (int)chunks, bc, os);
+    else hipLaunchKernelGGL((score_max_kernel<DT, LAYOUT, D, false, true>), g, b, 0, s, a, (int)chunks, bc, os);
+  } else if (a.hist) {
+    hipLaunchKernelGGL((score_max_kernel<DT, LAYOUT, D, true, false>), g, b, 0, s, a, (int)chunks, bc, os);
+  } else {
+    hipLaunchKernelGGL((score_max_kernel<DT, LAYOUT, D, false, false>), g, b, 0, s, a, (int)chunks, bc, os);
+  }
   return hipGetLastError();
 }
 

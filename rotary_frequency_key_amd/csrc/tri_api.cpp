@@ -240,7 +240,6 @@ int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, 
   tri::OffsetSet os;
   const int so = parse_offsets(offsets, n_offsets, &os);
   if (so != TRI_OK) return so;
-  if ((layout & TRI_KEYS_ROTATED) != 0) return TRI_ERR_UNSUPPORTED;
   void* hist = nullptr;
   if (ws_bytes != nullptr) {
     if (*ws_bytes < need) return TRI_ERR_WORKSPACE;
@@ -251,8 +250,8 @@ int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, 
   if (st != TRI_OK) return st;
   tri::BandConst bc;
   band_constants(d, theta, &bc);
-  tri::ScoreArgs a{keys, dtype, layout, d, false, row_off, n_units, total_rows, max_rows,
-                   pos, t_now, centers, scores, static_cast<uint32_t*>(hist)};
+  tri::ScoreArgs a{keys, dtype, layout & ~TRI_KEYS_ROTATED, d, (layout & TRI_KEYS_ROTATED) != 0, row_off, n_units,
+                   total_rows, max_rows, pos, t_now, centers, scores, static_cast<uint32_t*>(hist)};
   if (tri::launch_score_max(a, bc, os, static_cast<hipStream_t>(stream)) != hipSuccess) return TRI_ERR_HIP;
   return TRI_OK;
 }
@@ -331,7 +330,6 @@ int tri_prune_pass_max(const void* K, const void* V, int dtype, int layout, int 
   tri::OffsetSet os;
   const int so = parse_offsets(offsets, n_offsets, &os);
   if (so != TRI_OK) return so;
-  if ((layout & TRI_KEYS_ROTATED) != 0) return TRI_ERR_UNSUPPORTED;
   return tri::prune_pass_run(K, V, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now,
                              centers, B, scores, kept_idx, kept_cnt, K_out, V_out, pos_out, ws,
                              ws_bytes != nullptr ? *ws_bytes : 0, false, static_cast<hipStream_t>(stream), &os);
@@ -372,8 +370,8 @@ int prune_pass_run(const void* K, const void* V, int dtype, int layout, int d, d
   if (os != nullptr) {  // the maximum over the offsets, from the raw centers, histogram into ws
     BandConst bc;
     band_constants(d, theta, &bc);
-    const ScoreArgs sa{K, dtype, layout, d, false, row_off, n_units, total_rows, max_rows, pos, t_now, mu, scores,
-                       static_cast<uint32_t*>(ws)};
+    const ScoreArgs sa{K, dtype, layout & ~TRI_KEYS_ROTATED, d, (layout & TRI_KEYS_ROTATED) != 0, row_off,
+                       n_units, total_rows, max_rows, pos, t_now, mu, scores, static_cast<uint32_t*>(ws)};
     if (launch_score_max(sa, bc, *os, s) != hipSuccess) return TRI_ERR_HIP;
   } else if (launch_score_call(K, dtype, layout, d, theta, row_off, n_units, total_rows, max_rows, pos, t_now, mu,
                                scores, ws, s) != hipSuccess) {

@@ -193,7 +193,8 @@ def test_prune_pass_max_argument_errors():
     assert _prune_max(offsets=[1, -1]) == ARG
     assert _prune_max(offsets=[1 << 24]) == ARG
     assert _prune_max(offsets=list(range(33))) == UNSUP
-    assert _prune_max(layout=0x100) == UNSUP  # rotated keys
+    assert _prune_max(layout=0x100, pos=None, po=None, d=96) == UNSUP  # rotated keys: no positions needed
+    assert _prune_max(layout=0x100, pos=None, po=None, Ko=A["keys"]) == ALIAS
     assert _prune_max(dtype=3) == ARG
     assert _prune_max(d=96) == UNSUP
     assert _prune_max(B=-1) == ARG
@@ -272,7 +273,9 @@ def test_score_max_argument_errors():
     assert _score_max(offsets=[1, -1]) == ARG
     assert _score_max(offsets=[1 << 24]) == ARG
     assert _score_max(offsets=list(range(33))) == UNSUP
-    assert _score_max(layout=0x100) == UNSUP  # rotated keys
+    # rotated keys need no positions: the call gets past that check to the next one
+    assert _score_max(layout=0x100, pos=None, d=96) == UNSUP
+    assert _score_max(layout=0x100, pos=None, scores=A["keys"] + 4096) == ALIAS
     assert _score_max(pos=None) == ARG
     assert _score_max(d=96) == UNSUP
     assert _score_max(scores=A["keys"] + 4096) == ALIAS

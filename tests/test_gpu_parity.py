@@ -490,6 +490,75 @@ def test_max_over_offsets(d, dtype, layout):
                worst, total, U)
 
 
+@pytest.mark.parametrize("d,dtype,layout", [(128, "bf16", 0), (128, "bf16", 1), (128, "f32", 0), (64, "f32", 0),
+                                             (256, "bf16", 0)])
+def test_max_over_offsets_rotated(d, dtype, layout):
+    """Keys stored after the rotary rotation, maximum over the offsets. conj(k) e^{i w (t - p + delta)}
+    = conj(k_rot) e^{i w (t + delta)}, so the reference is the oracle's literal loop on the stored
+    keys with every distance equal to t. d = 128 is a bf16 matrix product of the key rows
+    themselves; the scores are computed without positions. Then the fused pass
+    (tri_prune_pass_max) against the three calls, bit for bit."""
+    import rotary_frequency_key_amd as tri
+    from tests._parity import kept_mismatch, keys_to_device, keys_to_host
+
+    wl = dataclasses.replace(workload("c2"), d=d, dtype=dtype, heads=3, theta=5e5)
+    P, _ = _rotated_case(wl, [0, 1, 2], [4000, 1500, 33], layout)
+    lay = "half_split" if layout & 1 else "interleaved"
+    F = d // 2
+    U, B = 3, 500
+    dev = torch.device("cuda:0")
+    K = keys_to_device(P["keys"], dtype, dev)
+    V = keys_to_device(P["values"], dtype, dev)
+    pos = torch.from_numpy(P["pos"]).to(dev)
+    row_off = torch.from_numpy(P["row_off"]).to(dev)
+    t = torch.from_numpy(P["t"]).to(dev)
+    centers = torch.from_numpy(np.ascontiguousarray(P["centers"], dtype=np.float32)).to(dev)
+    omega = O.rotary_frequencies(d, wl.theta)
+    rot = layout | tri.TRI_KEYS_ROTATED
+    sets = [O.power_of_two_offsets(), np.array([0, 3, 17, 1000, 99991], dtype=np.int64)]
+    if d == 128:
+        sets.append(np.arange(32, dtype=np.int64) * 977 + 5)
+    for offsets in sets:
+        say(f"case max over offsets, rotated keys, d={d} {dtype} layout={layout} |D|={offsets.size}")
+        ws = tri.make_workspace(U, 4000, dev)
+        scores = tri.tri_score_max(K, row_off, 4000, None, t, centers, wl.theta, offsets, layout=rot, ws=ws)
+        kept_idx, kept_cnt = tri.tri_select_topb(scores, row_off, 4000, B, ws=ws, hist_from_score=True)
+        K_out, V_out, pos_out = tri.tri_compact_kv(K, V, pos, row_off, kept_idx, kept_cnt, B)
+        wsf = tri.make_workspace(U, 4000, dev)
+        fused = tri.prune_pass_max(K, V, pos, row_off, 4000, t, centers, wl.theta, offsets, B, ws=wsf, layout=rot)
+        torch.cuda.synchronize()
+        for x, y, name in zip(fused[:3], (scores, kept_idx, kept_cnt), ("scores", "kept_idx", "kept_cnt")):
+            assert torch.equal(x, y), f"fused pass: {name}"
+        cnt = kept_cnt.cpu().numpy()
+        for x, y, name in zip(fused[3:], (K_out, V_out, pos_out), ("K_out", "V_out", "pos_out")):
+            xb, yb = x.cpu(), y.cpu()
+            if xb.dtype == torch.bfloat16:
+                xb, yb = xb.view(torch.int16), yb.view(torch.int16)
+            for i in range(U):
+                assert torch.equal(xb[i, :cnt[i]], yb[i, :cnt[i]]), f"fused pass: {name}, unit {i}"
+        assert ws_rest(ws) and ws_rest(wsf)
+        s_gpu = scores.cpu().numpy()
+        kept_all, K_host = kept_idx.cpu().numpy(), keys_to_host(K_out, dtype)
+        worst, total = 0.0, 0
+        for i in range(U):
+            a, b = P["row_off"][i], P["row_off"][i + 1]
+            ks = O.as_bands(widen(P["keys"][a:b], dtype), lay)  # the stored keys, as the kernel reads them
+            cb = O.as_bands(P["centers"][i].astype(np.float64))
+            dist = O.distances(int(P["t"][i]), np.zeros(b - a, dtype=np.int32))
+            s_ref = O.score_unfolded_max(cb, ks, dist, omega, offsets)
+            scale = np.sum(np.abs(cb)[None, :] * np.abs(ks), axis=1) / F
+            err = score_error(s_gpu[a:b], s_ref, scale)
+            say(f"   unit {i}: max score error {err:.3g}")
+            assert err <= TOL, err
+            m = min(B, b - a)
+            kept = kept_all[i, :m]
+            assert np.array_equal(kept, O.select_topb(s_gpu[a:b], B))
+            worst, total = max(worst, err), total + kept_mismatch(kept, s_ref, scale, B)
+            assert np.array_equal(K_host[i, :m], P["keys"][a:b][kept])
+        margin(f"max over offsets, rotated keys (d={d}, {dtype}, {'half-split' if layout else 'interleaved'}, "
+               f"|D|={offsets.size})", worst, total, U)
+
+
 def ws_rest(ws):
     return bool(np.all(ws[:3 * 4096 * 4].cpu().numpy() == 0))
 
