@@ -441,8 +441,10 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a
 // P_{f(e), o}, e the element of the row and f(e) its band. There is no per-key trigonometry: bf16
 // keys are exact bf16 operands (W split into hi + lo: two products per step), fp32 keys are split
 // like W (three). Lane L holds key L % 16 and, at step s, elements 32 s + 8 (L / 16) + i of it:
-// one 16-byte piece of the row for bf16, two for fp32. W, the result and the stores are as in
-// score_max_mfma_kernel.
+// one 16-byte piece of the row for bf16, two for fp32. Loaded in that layout, one instruction would
+// read 64 bytes from each of 16 rows; the tiles are loaded contiguously instead (1 KB per
+// instruction) and pass through a per-wave LDS region into the operand layout. W, the result and
+// the stores are as in score_max_mfma_kernel.
 template <int DT, int LAYOUT, bool HIST, int NT>  // NT: tiles of 16 offsets
 __global__ __launch_bounds__(kMaxThreads) void score_max_rot_mfma_kernel(ScoreArgs a, int chunks_per_unit,
                                                                          BandConst bc, OffsetSet os) {
@@ -459,6 +461,8 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_rot_mfma_kernel(ScoreAr
   static_assert(ITERS > PF, "tiles per wave");
 
   __shared__ __align__(16) bf16x8 wsh[NT][4][2][64];  // W for each lane: [tile][step][hi, lo][lane]
+  constexpr uint32_t TSTRIDE = ROW_BYTES + 16;  // LDS bytes per staged row (16 of padding)
+  __shared__ __align__(16) char tile[WAVES][16 * TSTRIDE];  // each wave's 16 rows, staged
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
 
   const int unit = blockIdx.x / chunks_per_unit;
@@ -480,14 +484,17 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_rot_mfma_kernel(ScoreAr
   const uint32_t wave_row = (uint32_t)(wave * 16 + mc);
   // a ring of PF + 1 tiles in registers (the loop is unrolled): tile it in use, it + 1 .. it + PF
   // in flight; with one tile ahead a CU keeps too few bytes in flight to cover the memory latency
-  u32x4 kq[PF + 1][4][PIECES];
+  // loads are contiguous: instruction g of a tile covers 1 KB, lane L the 16 bytes at
+  // g * 1024 + 16 L of the wave's 16 rows; the tile then goes through LDS into the operand layout
+  constexpr int LPT = 16 * ROW_BYTES / 1024;  // load instructions per tile
+  u32x4 kq[PF + 1][LPT];
   auto load_tile = [&](int j, int slot) {
-    const uint32_t row = min(wave_row + (uint32_t)(j * ROWS_ITER), last);
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int q = 0; q < PIECES; ++q)
-        kq[slot][st][q] = ld_stream<u32x4>(kbase, row * ROW_BYTES + (uint32_t)((32 * st + 8 * mq) * EB + 16 * q));
+    for (int g = 0; g < LPT; ++g) {
+      const uint32_t byte = (uint32_t)(g * 1024 + 16 * lane);
+      const uint32_t row = min((uint32_t)(j * ROWS_ITER + wave * 16) + byte / ROW_BYTES, last);
+      kq[slot][g] = ld_stream<u32x4>(kbase, row * ROW_BYTES + byte % ROW_BYTES);
+    }
   };
 #pragma unroll
   for (int j = 0; j < PF; ++j) load_tile(j, j);
@@ -548,7 +555,26 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_rot_mfma_kernel(ScoreAr
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     if (it + PF < ITERS) load_tile(it + PF, (it + PF) % (PF + 1));
-    const auto& kc = kq[it % (PF + 1)];
+    // stage the tile, then read it in the operand layout (the wave's own region: its LDS
+    // operations run in order; the fences keep the compiler's order too)
+    char* tw = tile[wave];
+#pragma unroll
+    for (int g = 0; g < LPT; ++g) {
+      const uint32_t byte = (uint32_t)(g * 1024 + 16 * lane);
+      *reinterpret_cast<u32x4*>(tw + (byte / ROW_BYTES) * TSTRIDE + byte % ROW_BYTES) = kq[it % (PF + 1)][g];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    u32x4 kc[4][PIECES];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int q = 0; q < PIECES; ++q)
+        kc[st][q] = *reinterpret_cast<const u32x4*>(tw + mc * TSTRIDE + (32 * st + 8 * mq) * EB + 16 * q);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     __builtin_amdgcn_sched_barrier(0);  // the next tile's loads stay in flight during this one
     f32x4m acc[NT];
 #pragma unroll
