@@ -559,6 +559,70 @@ def test_max_over_offsets_rotated(d, dtype, layout):
                f"|D|={offsets.size})", worst, total, U)
 
 
+def test_max_pass_edge_cases():
+    """The max-over-offsets pass on empty, one-row, tail-sized and multi-chunk units (up to 70000
+    rows, beyond 2^16) in one launch, budgets 0, 1, 600 and above every unit, plain and rotated
+    keys: the fused pass bit for bit against the three calls, both workspaces back at rest, the
+    scores against the oracle's literal loop and the kept set the top-B of the GPU's scores."""
+    import rotary_frequency_key_amd as tri
+    from tests._parity import keys_to_device
+
+    wl = workload("c2")
+    lengths = [0, 1, 5, 511, 513, 4100, 70000]
+    U, max_rows = len(lengths), max(lengths)
+    P = pack_units(dataclasses.replace(wl, heads=U), list(range(U)), lengths, workers=gen_workers())
+    dev = torch.device("cuda:0")
+    K, V = keys_to_device(P["keys"], "bf16", dev), keys_to_device(P["values"], "bf16", dev)
+    pos = torch.from_numpy(P["pos"]).to(dev)
+    row_off = torch.from_numpy(P["row_off"]).to(dev)
+    t = torch.from_numpy(P["t"]).to(dev)
+    centers = torch.from_numpy(np.ascontiguousarray(P["centers"], dtype=np.float32)).to(dev)
+    offsets = O.power_of_two_offsets()
+    omega = O.rotary_frequencies(wl.d, wl.theta)
+    F = wl.d // 2
+    hist_words = U * 4096
+    for layout in [0, tri.TRI_KEYS_ROTATED]:
+        checked = False
+        for B in [0, 1, 600, 80000]:
+            say(f"case max pass edge units layout={layout:#x} B={B}")
+            ws = tri.make_workspace(U, max_rows, dev)
+            scores = tri.tri_score_max(K, row_off, max_rows, pos, t, centers, wl.theta, offsets, layout=layout, ws=ws)
+            kept_idx, kept_cnt = tri.tri_select_topb(scores, row_off, max_rows, B, ws=ws, hist_from_score=True)
+            K_out, V_out, pos_out = tri.tri_compact_kv(K, V, pos, row_off, kept_idx, kept_cnt, B)
+            wsf = tri.make_workspace(U, max_rows, dev)
+            fused = tri.prune_pass_max(K, V, pos, row_off, max_rows, t, centers, wl.theta, offsets, B, ws=wsf,
+                                       layout=layout)
+            torch.cuda.synchronize()
+            for x, y, name in zip(fused[:3], (scores, kept_idx, kept_cnt), ("scores", "kept_idx", "kept_cnt")):
+                assert torch.equal(x, y), f"fused pass: {name}"
+            cnt = kept_cnt.cpu().numpy()
+            for x, y, name in zip(fused[3:], (K_out, V_out, pos_out), ("K_out", "V_out", "pos_out")):
+                xb, yb = x.cpu(), y.cpu()
+                if xb.dtype == torch.bfloat16:
+                    xb, yb = xb.view(torch.int16), yb.view(torch.int16)
+                for i in range(U):
+                    assert torch.equal(xb[i, :cnt[i]], yb[i, :cnt[i]]), f"fused pass: {name}, unit {i}"
+            for w in (ws, wsf):
+                assert bool(np.all(w[:hist_words * 4].cpu().numpy() == 0))
+            s_gpu = scores.cpu().numpy()
+            kept_all = kept_idx.cpu().numpy()
+            for i in range(U):
+                a, b = P["row_off"][i], P["row_off"][i + 1]
+                m = min(B, b - a)
+                assert cnt[i] == m
+                assert np.array_equal(kept_all[i, :m], O.select_topb(s_gpu[a:b], B))
+                assert np.all(kept_all[i, m:] == -1)
+                if not checked and b > a:  # the scores do not depend on B: against the oracle once
+                    kb = O.as_bands(widen(P["keys"][a:b], "bf16"))
+                    cb = O.as_bands(P["centers"][i].astype(np.float64))
+                    p_eff = np.zeros(b - a, dtype=np.int32) if layout else P["pos"][a:b]
+                    s_ref = O.score_unfolded_max(cb, kb, O.distances(int(P["t"][i]), p_eff), omega, offsets)
+                    scale = np.sum(np.abs(cb)[None, :] * np.abs(kb), axis=1) / F
+                    err = score_error(s_gpu[a:b], s_ref, scale)
+                    assert err <= TOL, (layout, i, err)
+            checked = True
+
+
 def ws_rest(ws):
     return bool(np.all(ws[:3 * 4096 * 4].cpu().numpy() == 0))
 
