@@ -203,7 +203,9 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_kernel(ScoreArgs a, int
 // are the lane's bands 16 h + 4 (L / 16) + j, four contiguous pieces of its key row: value i of
 // step s is band n = 8 (s & 1) + i of that list (n = 4 h + j), its real part for s < 2 and its
 // imaginary part for s >= 2. W's columns use the same order; the waves of a workgroup build W once
-// in LDS and each keeps it in registers. Offsets past the last repeat it (the maximum does not
+// in LDS and each keeps it in registers. bf16 interleaved keys are loaded contiguously (1 KB per
+// instruction) and pass through a per-wave LDS region into that layout; loaded in it directly,
+// one instruction would read 64 bytes from each of 16 rows. Offsets past the last repeat it (the maximum does not
 // change). The result gives lane L key L % 16 at offsets 16 t + 4 (L / 16) + i of tile t: the
 // maximum over those, then over the key's four lanes (two lane swaps), finishes the key.
 
@@ -240,6 +242,10 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a
   using KT = typename L::T;
 
   __shared__ __align__(16) bf16x8 wsh[NT][4][2][64];  // W for each lane: [tile][step][hi, lo][lane]
+  // bf16 interleaved keys: tiles loaded contiguously (1 KB per instruction), staged per wave
+  constexpr bool STAGE = DT == kDtBf16 && LAYOUT == kInterleaved;
+  constexpr uint32_t TSTRIDE = 256 + 16;
+  __shared__ __align__(16) char tile[STAGE ? WAVES : 1][STAGE ? 16 * TSTRIDE : 16];
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
 
   const int unit = blockIdx.x / chunks_per_unit;
@@ -261,13 +267,24 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a
   const uint32_t last = (uint32_t)(r1 - r0 - 1);
   const uint32_t wave_row = (uint32_t)(wave * 16 + mc);
   KT kb[4];
+  u32x4 kr[4];  // STAGE: the lane's 16 bytes at g * 1024 + 16 lane of the wave's 16 rows
   int32_t pb;
-  {
-    const uint32_t row = min(wave_row, last);
+  auto load_next = [&](int j) {
+    const uint32_t row = min(wave_row + (uint32_t)(j * ROWS_ITER), last);
+    if constexpr (STAGE) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) kb[h] = L::load(kbase, row, 4 * h + mq);
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t byte = (uint32_t)(g * 1024 + 16 * lane);
+        const uint32_t r = min((uint32_t)(j * ROWS_ITER + wave * 16) + byte / 256u, last);
+        kr[g] = ld_stream<u32x4>(kbase, r * 256u + byte % 256u);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) kb[h] = L::load(kbase, row, 4 * h + mq);
+    }
     pb = load_pos(pbase, row);
-  }
+  };
+  load_next(0);
 
   if constexpr (HIST) {
     for (int i = threadIdx.x; i < kHistBins; i += kMaxThreads) lhist[i] = 0u;
@@ -342,15 +359,30 @@ __global__ __launch_bounds__(kMaxThreads) void score_max_mfma_kernel(ScoreArgs a
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     KT kc[4];
+    if constexpr (STAGE) {
+      char* tw = tile[wave];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) kc[h] = kb[h];
-    const int32_t pc = pb;
-    if (it + 1 < ITERS) {
-      const uint32_t row = min(wave_row + (uint32_t)((it + 1) * ROWS_ITER), last);
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t byte = (uint32_t)(g * 1024 + 16 * lane);
+        *reinterpret_cast<u32x4*>(tw + (byte / 256u) * TSTRIDE + byte % 256u) = kr[g];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int h = 0; h < 4; ++h) kb[h] = L::load(kbase, row, 4 * h + mq);
-      pb = load_pos(pbase, row);
+      for (int h = 0; h < 4; ++h) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tw + mc * TSTRIDE + (4 * h + mq) * 16);
+        kc[h] = KT{{v.x, v.y, v.z, v.w}};
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) kc[h] = kb[h];
     }
+    const int32_t pc = pb;
+    if (it + 1 < ITERS) load_next(it + 1);
     __builtin_amdgcn_sched_barrier(0);  // the next tile's loads stay in flight during this one
     // operand B: conj(k_f) e^{i w_f Delta} of row mc, k laid out as in W
     const uint32_t dl = (uint32_t)(t - pc);
