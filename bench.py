@@ -573,6 +573,8 @@ def main():
     del copies, plans
     torch.cuda.empty_cache()
     if not args.no_large:
+        result["units_sweep"] = units_sweep(tri, torch, dev, args, copy_gbps)
+        torch.cuda.empty_cache()
         for name in LARGE_WORKLOADS:
             result[name] = large_workload(tri, torch, dev, args, name)
             result[name]["frac_of_copy"] = result[name]["hbm_gbps"] / copy_gbps
@@ -644,6 +646,62 @@ def timeline(tri, torch, dev, step, n_passes):
         for j in range(1, 6):
             out.append(f"| {names[j - 1]} | {np.median(full[:, j] - full[:, j - 1]):.2f} |")
     return "\n".join(out)
+
+
+def units_sweep(tri, torch, dev, args, copy_gbps, layers=(1, 2, 4, 8, 16, 32)):
+    """The same pass on 1..32 layers of the one-layer workload (8 KV heads x 32768 bf16 keys each,
+    B = 2048) in one tri_prune_pass call: where the pass stops being bound by its launches and
+    dependent round trips and becomes bound by bandwidth. Inputs generated on the device; passes
+    rotate over enough copies to hold more than 512 MB of K and V, beyond the Infinity Cache."""
+    import dataclasses
+
+    from synthgen import workload
+    from synthgen.device import device_workload
+
+    base = workload("c2")
+    out = []
+    for L in layers:
+        wl = dataclasses.replace(base, layers=L)
+        U, B = wl.n_units, wl.budget
+        per_copy = U * wl.n_keys * wl.d * wl.elem_bytes * 2
+        n_copies = max(1, -(-(512 << 20) // per_copy))
+        plans, keep = [], []
+        for ci in range(n_copies):
+            W = device_workload(dataclasses.replace(wl, seed=wl.seed + ci), dev)
+            R = int(W["row_off"][-1])
+            max_rows = int(W["lengths"].max())
+            _, mu = tri.tri_fold_weights(wl.d, wl.theta, np.array([1 << j for j in range(17)]), W["centers"])
+            bufs = dict(ws=tri.make_workspace(U, max_rows, dev),
+                        scores=torch.empty(R, dtype=torch.float32, device=dev),
+                        kept_idx=torch.empty((U, B), dtype=torch.int32, device=dev),
+                        kept_cnt=torch.empty(U, dtype=torch.int32, device=dev),
+                        K_out=torch.empty((U, B, wl.d), dtype=torch.bfloat16, device=dev),
+                        V_out=torch.empty((U, B, wl.d), dtype=torch.bfloat16, device=dev),
+                        pos_out=torch.empty((U, B), dtype=torch.int32, device=dev))
+            mu_d = torch.from_numpy(mu).to(dev)
+            plans.append(tri.PassPlan(W["K"], W["V"], W["pos"], W["row_off_d"], max_rows, W["t_d"], mu_d, wl.theta,
+                                      B, **bufs))
+            keep.append((W, bufs, mu_d))
+        steps = max(20, min(200, 4000 // L))
+        for i in range(2 * n_copies + 3):
+            plans[i % n_copies].run()
+        torch.cuda.synchronize()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
+        for i in range(steps):
+            plans[i % n_copies].run()
+        eb.record()
+        torch.cuda.synchronize()
+        us = ea.elapsed_time(eb) * 1e3 / steps
+        alg_total = sum(algorithmic_bytes(wl, R, U).values())
+        gbps = alg_total / (us * 1e-6) / 1e9
+        out.append({"layers": L, "units": U, "keys": R, "copies": n_copies, "us_per_pass": us,
+                    "keys_per_s": R / (us * 1e-6), "hbm_frac_of_peak": gbps / HBM_PEAK_GBPS,
+                    "frac_of_copy": gbps / copy_gbps})
+        del plans, keep
+        torch.cuda.empty_cache()
+    return {"note": "one tri_prune_pass over L layers of 8 KV heads x 32768 bf16 keys (B = 2048); inputs "
+                    "generated on the device", "passes": out}
 
 
 def large_workload(tri, torch, dev, args, name):
