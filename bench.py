@@ -594,7 +594,7 @@ def main():
 # 256 MB Infinity Cache, so no copies rotate.
 LARGE_WORKLOADS = {
     "all_layers": ("c3", "36 layers x 8 KV heads x 32768 keys (Qwen3-8B shape), bf16, B=2048, "
-                         "10% flat heads; 256 units or more: one select workgroup per unit"),
+                         "10% flat heads; 48 units or more: one select workgroup per unit"),
     "ragged_batch": ("c4", "16 sequences x 32 layers x 8 KV heads (Llama-3-8B shape), 8192..65536 keys "
                            "per sequence, bf16, B=2048"),
     "chat_pass0": ("c5", "4 sequences x 64 layers x 8 KV heads (Qwen3-32B shape), 131072 + 1024 keys, "

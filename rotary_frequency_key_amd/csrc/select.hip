@@ -14,7 +14,7 @@
 // Three arrangements of the same select, chosen on the host from the unit count and max_rows
 // (all give the same bits):
 //
-//  * Units of up to 64Ki rows, 256 units or more (many layers in one call):
+//  * Units of up to 64Ki rows, 48 units or more (a few layers or more in one call):
 //      topb_kernel -> compact_kernel
 //    One workgroup per unit with the keys in registers; the units alone fill the GPU.
 //  * Otherwise, units of up to 2^18 rows whose output slots make at most kFinishMaxWorkgroups
@@ -1090,7 +1090,11 @@ hipError_t launch_move(const SelectArgs& a, const MoveArgs& mv, hipStream_t s) {
 constexpr int kTN = 1024;
 constexpr int kTW = kTN / 64;
 constexpr int64_t kTopbMaxRows = 64 * kTN;
-constexpr int kTopbMinUnits = 256;  // tri_select_topb and tri_prune_pass use it from this many units on
+// tri_select_topb and tri_prune_pass use it from this many units on. Measured against candidates
+// + finish on units of 32768 keys, B = 2048 (pass time per call): 8 units 33.6 against 26.9 us,
+// 16 units 48.3 against 42.3, 24 units 60.7 against 59.2, 32 units 74.4-75.8 against 73.4-77.1,
+// 64 units 128.3 against 138.6, 128 units 243.1 against 274.2, 192 units 376.2 against 406.9.
+constexpr int kTopbMinUnits = 48;
 
 struct TopbShared {
   uint32_t sh[4 * kTW];

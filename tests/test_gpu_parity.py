@@ -175,7 +175,7 @@ def test_granules_beyond_2_22_rows():
 
 
 def test_many_units_one_workgroup_select():
-    """264 ragged units (empty, one row, tails, up to 20000 rows): from 256 units on, the select
+    """264 ragged units (empty, one row, tails, up to 20000 rows): from 48 units on, the select
     holds each unit's keys in one workgroup and the compaction runs as its own kernel. Its
     results equal those of the fused resolve-and-emit path (max_rows above 64Ki) bit for bit,
     and sampled units match the oracle."""
@@ -206,8 +206,8 @@ def test_candidate_workgroups_with_several_chunks(n_units):
     """With max_rows above 2^18 a unit has 257 candidate chunks of 1024 rows; past 16384 chunks in
     all, one candidate workgroup takes several consecutive chunks of its unit (4 for 130 units,
     16 for 520). Ragged units end inside a chunk and inside a workgroup's run of chunks. The
-    results equal the bits of the one-chunk resolve path (130 units) or of the one-workgroup-per-
-    unit select (520), and sampled units match the oracle."""
+    results equal the bits of the one-workgroup-per-unit select (both unit counts are 48 or
+    more), and sampled units match the oracle."""
     wl = workload("c2")
     pattern = [0, 1, 1023, 1024, 1025, 2049, 3000, 4097, 5000, 700]
     lengths = (pattern * (n_units // len(pattern) + 1))[:n_units]
