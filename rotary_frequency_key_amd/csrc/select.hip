@@ -1094,7 +1094,12 @@ constexpr int64_t kTopbMaxRows = 64 * kTN;
 // + finish on units of 32768 keys, B = 2048 (pass time per call): 8 units 33.6 against 26.9 us,
 // 16 units 48.3 against 42.3, 24 units 60.7 against 59.2, 32 units 74.4-75.8 against 73.4-77.1,
 // 64 units 128.3 against 138.6, 128 units 243.1 against 274.2, 192 units 376.2 against 406.9.
+// With B = 256 (4 finish workgroups per unit) candidates + finish stay ahead a little longer:
+// 48 units 86.5 against 88.3 us, 64 units 111.8 against 112.4, 128 units 215.8 against 211.0; with
+// B = 8192 the one-workgroup select is ahead from 48 units (156.2 against 163.5). So it also needs
+// kTopbMinFinishGroups output groups of 64 slots in all.
 constexpr int kTopbMinUnits = 48;
+constexpr int64_t kTopbMinFinishGroups = 384;
 
 struct TopbShared {
   uint32_t sh[4 * kTW];
@@ -1258,15 +1263,16 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   if (!a.hist_ready && hpu > 0)
     hipLaunchKernelGGL(hist_kernel, dim3((unsigned)(U * hpu)), dim3(kHN), 0, s, a, (int)hpu);
-  if (a.max_rows <= kTopbMaxRows && a.n_units >= kTopbMinUnits) {  // one workgroup per unit fills the GPU
+  const int64_t mm = a.B < a.max_rows ? a.B : a.max_rows;
+  const int64_t fin_wgs = (int64_t)a.n_units * (mm > 0 ? (mm + kFinSlots - 1) / kFinSlots : 1);
+  if (a.max_rows <= kTopbMaxRows && a.n_units >= kTopbMinUnits && fin_wgs >= kTopbMinFinishGroups) {
+    // one workgroup per unit: the units' selects fill the GPU
     hipError_t e = launch_topb<false>(a, InplaceOut{nullptr, nullptr, 0u}, s);
     if (e != hipSuccess || a.K_out == nullptr) return e;
     const CompactArgs c{a.K, a.V, a.pos, a.row_bytes, a.row_off, a.n_units, a.total_rows, a.kept_idx, a.kept_cnt,
                         a.B, a.K_out, a.V_out, a.pos_out};
     return launch_compact(c, s);
   }
-  const int64_t mm = a.B < a.max_rows ? a.B : a.max_rows;
-  const int64_t fin_wgs = (int64_t)a.n_units * (mm > 0 ? (mm + kFinSlots - 1) / kFinSlots : 1);
   if (a.max_rows <= kFinishMaxRows && fin_wgs <= kFinishMaxWorkgroups) {
     hipError_t e = launch_cand(a, 1, s);
     if (e != hipSuccess) return e;

@@ -175,13 +175,14 @@ def test_granules_beyond_2_22_rows():
 
 
 def test_many_units_one_workgroup_select():
-    """264 ragged units (empty, one row, tails, up to 20000 rows): from 48 units on, the select
-    holds each unit's keys in one workgroup and the compaction runs as its own kernel. Its
-    results equal those of the fused resolve-and-emit path (max_rows above 64Ki) bit for bit,
-    and sampled units match the oracle."""
+    """396 ragged units (empty, one row, tails, up to 20000 rows): from 48 units and 384 groups of
+    64 output slots on (every budget here, B = 0 and 1 included), the select holds each unit's
+    keys in one workgroup and the compaction runs as its own kernel. Its results equal those of
+    the fused resolve-and-emit path (max_rows above 64Ki) bit for bit, and sampled units match
+    the oracle."""
     wl = workload("c2")
     pattern = [0, 1, 5, 511, 512, 513, 2049, 4100, 20000, 300, 64]
-    lengths = pattern * 24
+    lengths = pattern * 36
     units = list(range(len(lengths)))
     P = pack_units(dataclasses.replace(wl, heads=len(lengths)), units, lengths, workers=gen_workers())
     for B in [0, 1, 300, 2048, 5000]:
@@ -197,7 +198,7 @@ def test_many_units_one_workgroup_select():
                 for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
                     assert np.array_equal(o2[k], out[k]), (B, path, k)
                 assert o2["ws_after"], (B, path)
-        for i in [0, 1, 3, 8, 19, 263]:
+        for i in [0, 1, 3, 8, 19, 263, 395]:
             check_unit(P, i, wl, out, B, label=f"many units B={B}")
 
 
@@ -207,7 +208,7 @@ def test_candidate_workgroups_with_several_chunks(n_units):
     all, one candidate workgroup takes several consecutive chunks of its unit (4 for 130 units,
     16 for 520). Ragged units end inside a chunk and inside a workgroup's run of chunks. The
     results equal the bits of the one-workgroup-per-unit select (both unit counts are 48 or
-    more), and sampled units match the oracle."""
+    more, with 384 output groups or more), and sampled units match the oracle."""
     wl = workload("c2")
     pattern = [0, 1, 1023, 1024, 1025, 2049, 3000, 4097, 5000, 700]
     lengths = (pattern * (n_units // len(pattern) + 1))[:n_units]
