@@ -202,6 +202,25 @@ def test_many_units_one_workgroup_select():
             check_unit(P, i, wl, out, B, label=f"many units B={B}")
 
 
+def test_six_layers_in_one_call():
+    """Six layers of the one-layer shape in one call (48 units of 32768 keys), the smallest unit
+    count at which the select may hold each unit's keys in one workgroup: with B = 2048 (1536
+    groups of 64 output slots) it does, with B = 256 (192 groups) the candidate and finish kernels
+    run. Both equal, bit for bit, the same pass taken through candidates and finish by a max_rows
+    above 64Ki, and sampled units match the oracle."""
+    wl = dataclasses.replace(workload("c2"), layers=6)
+    P = pack_units(wl, workers=gen_workers())
+    for B in [256, 2048]:
+        say(f"case six layers in one call B={B}")
+        out = run_gpu(P, wl, B)
+        ref = run_gpu(P, wl, B, max_rows=65537)
+        for k in ["scores", "kept_idx", "kept_cnt", "K_out", "V_out", "pos_out"]:
+            assert np.array_equal(out[k], ref[k]), (B, k)
+        assert out["ws_after"] and ref["ws_after"]
+        for i in [0, 9, 30, 47]:
+            check_unit(P, i, wl, out, B, label=f"six layers B={B}")
+
+
 @pytest.mark.parametrize("n_units", [130, 520])
 def test_candidate_workgroups_with_several_chunks(n_units):
     """With max_rows above 2^18 a unit has 257 candidate chunks of 1024 rows; past 16384 chunks in
