@@ -216,8 +216,8 @@ int tri_score_max(const void* keys, int dtype, int layout, int d, double theta, 
  *   digits resolved among the keys of the threshold's top-digit bin; then the kept indices are
  *   written in order. The arrangement depends on the shape, not the result: with 48 units or
  *   more of up to 2^16 rows and at least 384 groups of 64 output slots in all
- *   (n_units * ceil(min(B, max_rows) / 64)), one workgroup per unit; otherwise, with units of up to 2^18 rows
- *   and at most 4096 groups of 64 output slots in all (n_units * ceil(min(B, max_rows) / 64)), a
+ *   (n_units * ceil(min(B, max_rows) / 64)), one workgroup per unit; otherwise, with units of up
+ *   to 2^18 rows and at most 4096 such groups, a
  *   candidate kernel (1024 rows per workgroup) and one kernel that resolves the threshold and
  *   writes 64 output slots per workgroup; every other shape takes separate candidate,
  *   threshold and output kernels.
@@ -256,8 +256,8 @@ int tri_compact_kv(const void* K, const void* V, const int32_t* pos, int dtype, 
  * tri_prune_pass - one whole pruning pass: tri_score, tri_select_topb and tri_compact_kv fused,
  * same results as calling the three in turn. Three launches for one layer's heads (score with
  * histogram; candidates; threshold with output and row gather) and for 48 units and more of
- * up to 2^16 rows with 384 output groups or more (score; select; row gather); four for the other shapes (score; candidates;
- * threshold; output with row gather), as in tri_select_topb.
+ * up to 2^16 rows with 384 output groups or more (score; select; row gather); four for the other
+ * shapes (score; candidates; threshold; output with row gather), as in tri_select_topb.
  *
  * Arguments are those of the three functions: K (the keys) and V as in tri_compact_kv, the
  * score arguments as in tri_score, B, kept_idx and kept_cnt as in tri_select_topb, K_out /

@@ -14,9 +14,12 @@
 // Three arrangements of the same select, chosen on the host from the unit count and max_rows
 // (all give the same bits):
 //
-//  * Units of up to 64Ki rows, 48 units or more (a few layers or more in one call):
+//  * Units of up to 64Ki rows, 48 units or more with 384 groups of 64 output slots or more (a few
+//    layers or more in one call):
 //      topb_kernel -> compact_kernel
-//    One workgroup per unit with the keys in registers; the units alone fill the GPU.
+//    One workgroup per unit with the keys in registers; from a few dozen units on, many units'
+//    selects run at once, and the other arrangement's resolve in every output workgroup costs
+//    more.
 //  * Otherwise, units of up to 2^18 rows whose output slots make at most kFinishMaxWorkgroups
 //    groups of 64 in all (a few layers' heads, budgets of a few thousand):
 //      cand_kernel -> finish_kernel
