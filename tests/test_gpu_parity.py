@@ -647,6 +647,68 @@ def ws_rest(ws):
     return bool(np.all(ws[:3 * 4096 * 4].cpu().numpy() == 0))
 
 
+def _top_digits(scores):
+    """Bits 31..20 of the key that orders binary32 scores as the select ranks them (descending,
+    -0 equal to +0, NaN below every number): NaN -> 0, +-0 -> 2^31, a positive score -> its bits
+    with the sign bit set, a negative score -> its bits inverted."""
+    b = scores.view(np.uint32).astype(np.uint64)
+    mag = b & 0x7FFFFFFF
+    key = np.where(b >> 31 == 1, (~b) & 0xFFFFFFFF, b | 0x80000000)
+    key = np.where(mag == 0, 0x80000000, key)
+    key = np.where(mag > 0x7F800000, 0, key)
+    return (key >> 20).astype(np.int64)
+
+
+@pytest.mark.parametrize("kind", ["folded", "rotated", "max"])
+def test_score_histogram_counts(kind):
+    """The top-digit histogram the score kernels add into the workspace (the select's first
+    radix digit) equals, per unit and bin, a count over the scores they return; a second call
+    adds the same counts again. Ragged units (0 to 20000 rows, tails inside a 1024-row chunk)
+    and one zero-center unit, whose scores are all +-0 (one bin)."""
+    import rotary_frequency_key_amd as tri
+    from tests._parity import keys_to_device
+
+    wl = workload("c2")
+    lengths = [0, 1, 5, 1023, 1025, 4100, 20000, 3000]
+    U = len(lengths)
+    P = pack_units(dataclasses.replace(wl, heads=U), list(range(U)), lengths)
+    P["centers"][7] = 0.0
+    dev = torch.device("cuda:0")
+    K = keys_to_device(P["keys"], wl.dtype, dev)
+    pos = torch.from_numpy(P["pos"]).to(dev)
+    row_off = torch.from_numpy(P["row_off"]).to(dev)
+    t = torch.from_numpy(P["t"]).to(dev)
+    max_rows = max(lengths)
+    _, mu = tri.tri_fold_weights(wl.d, wl.theta, O.power_of_two_offsets(), P["centers"])
+    mu_d = torch.from_numpy(mu).to(dev)
+    centers = torch.from_numpy(np.ascontiguousarray(P["centers"], dtype=np.float32)).to(dev)
+    ws = torch.zeros(U * 4096 * 4, dtype=torch.uint8, device=dev)
+    say(f"case score histogram counts, {kind}")
+
+    def call():
+        if kind == "folded":
+            return tri.tri_score(K, row_off, max_rows, pos, t, mu_d, wl.theta, ws=ws)
+        if kind == "rotated":  # the same stored rows read as rotated keys
+            return tri.tri_score(K, row_off, max_rows, None, t, mu_d, wl.theta,
+                                 layout=tri.TRI_KEYS_ROTATED, ws=ws)
+        return tri.tri_score_max(K, row_off, max_rows, pos, t, centers, wl.theta, O.power_of_two_offsets(), ws=ws)
+
+    scores = call().cpu().numpy()
+    torch.cuda.synchronize()
+    h1 = ws.view(torch.int32).cpu().numpy().reshape(U, 4096).astype(np.int64)
+    expect = np.zeros((U, 4096), dtype=np.int64)
+    for u in range(U):
+        a, b = int(P["row_off"][u]), int(P["row_off"][u + 1])
+        expect[u] = np.bincount(_top_digits(scores[a:b]), minlength=4096)
+    assert np.array_equal(h1, expect)
+    assert expect[7, 2048] == lengths[7]  # the zero-center unit: every score +-0
+    again = call().cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(again.view(np.uint32), scores.view(np.uint32))
+    h2 = ws.view(torch.int32).cpu().numpy().reshape(U, 4096).astype(np.int64)
+    assert np.array_equal(h2, 2 * expect)
+
+
 def test_half_split_layout_matches_interleaved():
     wl = workload("c2")
     P = pack_units(wl, [2, 6], [4000, 777])
