@@ -810,7 +810,18 @@ def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
         append()
         plan.run()
     torch.cuda.synchronize()
-    evs = []
+    def moved_rows():
+        # rows the pass just run moved: its kept rows at or past row B (each moves to a freed slot
+        # below B). From its scores (row order before the moves): the B-th largest score T per
+        # unit; rows above T are kept, rows equal to T lowest row first up to B in all.
+        sc = plan_scores.view(U, C)
+        T = torch.topk(sc, B, dim=1).values[:, -1:]
+        gt, eq = sc > T, sc == T
+        need = B - gt.sum(dim=1)
+        ties_kept = torch.minimum(need, eq.sum(dim=1))
+        return (gt[:, B:].sum(dim=1) + (ties_kept - eq[:, :B].sum(dim=1)).clamp(min=0)).sum()
+
+    evs, moves = [], []
     for _ in range(steps):
         append()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -818,23 +829,18 @@ def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
         plan.run()
         e1.record()
         evs.append((e0, e1))
+        moves.append(moved_rows())  # after e1: outside the timed pass
     torch.cuda.synchronize()
     us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
-    # rows moved by the last pass: its kept rows at or past row B (each moves to a freed slot
-    # below B). From the last pass's scores (row order before the moves): the B-th largest score T
-    # per unit; rows above T are kept, rows equal to T lowest row first up to B in all.
-    sc = plan_scores.view(U, C)
-    T = torch.topk(sc, B, dim=1).values[:, -1:]
-    gt, eq = sc > T, sc == T
-    need = B - gt.sum(dim=1)
-    ties_kept = torch.minimum(need, eq.sum(dim=1))
-    moved = int((gt[:, B:].sum(dim=1) + (ties_kept - eq[:, :B].sum(dim=1)).clamp(min=0)).sum().item())
+    per_pass = [int(m.item()) for m in moves]
+    moved = float(np.mean(per_pass))
     rows = U * C
     # algorithmic bytes: every key row and position read, each moved row's K, V and position
     # read and written
     moved_bytes = moved * (2 * wl.d * 2 + 4) * 2
     return {"units": U, "rows_per_unit": C, "budget": B, "chunk": chunk, "us_per_pass": us,
             "keys_per_s": rows / (us * 1e-6), "moved_rows": moved,
+            "moved_rows_range": [min(per_pass), max(per_pass)],
             "algorithmic_gbps": (rows * (wl.d * 2 + 4) + moved_bytes) / (us * 1e-6) / 1e9,
             "note": f"{base_units} generated units tiled {replicas}x; chunk copy untimed"}
 
