@@ -763,22 +763,26 @@ def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
 
     The cache is synthetic: base_units units are generated (keys around a center as in every
     workload, B positions drawn without replacement from 0..131071, then 1024 new ones) and
-    tiled replicas times on the device, 2048 units in all. Before each timed pass a fresh chunk
-    is copied into rows B.. of every unit (untimed, events bracket the pass only)."""
+    tiled replicas times on the device, 2048 units in all. Before pass i the next of n_pool
+    generated chunks is copied into rows B.. of every unit, at positions 131072 + 1024 i onward,
+    and the current position moves to the end of that chunk, as in a prefill loop (untimed,
+    events bracket the pass only)."""
     from synthgen import unit_inputs, workload
 
     wl = workload("c5")
     B = wl.budget
     C = B + chunk
+    n_pool = 4
     t_now = 131072 + chunk
     Ks, Vs, Ps, Cs, pool_k, pool_v = [], [], [], [], [], []
     for u in range(base_units):
-        x = unit_inputs(wl, u, C + chunk)  # C rows for the cache, one more chunk for the pool
+        x = unit_inputs(wl, u, C + n_pool * chunk)  # C rows for the cache, then the chunks
         rng = np.random.default_rng([wl.seed, 0xC5, u])
         old = np.sort(rng.choice(131072, size=B, replace=False)).astype(np.int32)
         Ks.append(x["keys"][:C]); Vs.append(x["values"][:C]); Cs.append(x["center"])
         Ps.append(np.concatenate([old, np.arange(131072, t_now, dtype=np.int32)]))
-        pool_k.append(x["keys"][C:]); pool_v.append(x["values"][C:])
+        pool_k.append(x["keys"][C:].reshape(n_pool, chunk, wl.d))
+        pool_v.append(x["values"][C:].reshape(n_pool, chunk, wl.d))
 
     def dev16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -787,9 +791,9 @@ def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
     K = dev16(np.stack(Ks)).repeat(replicas, 1, 1).reshape(U * C, wl.d)
     V = dev16(np.stack(Vs)).repeat(replicas, 1, 1).reshape(U * C, wl.d)
     pos = torch.from_numpy(np.stack(Ps)).to(dev).repeat(replicas, 1).reshape(U * C)
-    chunk_k = dev16(np.stack(pool_k)).repeat(replicas, 1, 1)
-    chunk_v = dev16(np.stack(pool_v)).repeat(replicas, 1, 1)
-    chunk_p = torch.arange(131072, t_now, dtype=torch.int32, device=dev).repeat(U, 1)
+    chunk_k = dev16(np.stack(pool_k)).repeat(replicas, 1, 1, 1)  # [U][n_pool][chunk][d]
+    chunk_v = dev16(np.stack(pool_v)).repeat(replicas, 1, 1, 1)
+    chunk_p = torch.arange(chunk, dtype=torch.int32, device=dev).repeat(U, 1)
     _, mu = tri.tri_fold_weights(wl.d, wl.theta, np.array([1 << j for j in range(17)]), np.stack(Cs))
     mu = torch.from_numpy(mu).to(dev).repeat(replicas, 1, 1).contiguous()
     row_off = torch.arange(0, (U + 1) * C, C, dtype=torch.int64, device=dev)
@@ -800,10 +804,15 @@ def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
                            kept_cnt=torch.empty(U, dtype=torch.int32, device=dev))
     K3, V3, P2 = K.view(U, C, wl.d), V.view(U, C, wl.d), pos.view(U, C)
 
+    passes = [0]
+
     def append():
-        K3[:, B:].copy_(chunk_k)
-        V3[:, B:].copy_(chunk_v)
-        P2[:, B:].copy_(chunk_p)
+        i = passes[0]
+        passes[0] += 1
+        K3[:, B:].copy_(chunk_k[:, i % n_pool])
+        V3[:, B:].copy_(chunk_v[:, i % n_pool])
+        P2[:, B:].copy_(chunk_p + (131072 + i * chunk))
+        t.fill_(131072 + (i + 1) * chunk)
 
     steps = max(3, min(args.steps, 20))
     for _ in range(2):
@@ -842,7 +851,8 @@ def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
             "keys_per_s": rows / (us * 1e-6), "moved_rows": moved,
             "moved_rows_range": [min(per_pass), max(per_pass)],
             "algorithmic_gbps": (rows * (wl.d * 2 + 4) + moved_bytes) / (us * 1e-6) / 1e9,
-            "note": f"{base_units} generated units tiled {replicas}x; chunk copy untimed"}
+            "note": f"{base_units} generated units tiled {replicas}x; a new chunk at the next positions "
+                    f"before each pass ({n_pool} generated chunks in turn), its copy untimed"}
 
 
 if __name__ == "__main__":
