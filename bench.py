@@ -756,6 +756,18 @@ def large_workload(tri, torch, dev, args, name):
             "note": "one tri_prune_pass; generated on the device"}
 
 
+def count_moved_rows(torch, sc, B):
+    """Rows an in-place pass moves, from its scores sc [U][C] (row order before the moves, C > B,
+    no NaN): its kept rows at or past row B, each of which moves to a freed slot below B. Per unit
+    the B-th largest score T; rows above T are kept, rows equal to T lowest row first up to B in
+    all. Returns a 0-d tensor on sc's device."""
+    T = torch.topk(sc, B, dim=1).values[:, -1:]
+    gt, eq = sc > T, sc == T
+    need = B - gt.sum(dim=1)
+    ties_kept = torch.minimum(need, eq.sum(dim=1))
+    return (gt[:, B:].sum(dim=1) + (ties_kept - eq[:, :B].sum(dim=1)).clamp(min=0)).sum()
+
+
 def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
     """Chat steady state (the 64-layer x 8-head x 4-sequence shape, B = 12000): every unit holds
     the B rows kept by earlier passes, at sparse positions below 131072, and a 1024-row prefill
@@ -820,15 +832,7 @@ def steady_state(tri, torch, dev, args, base_units=32, replicas=64, chunk=1024):
         plan.run()
     torch.cuda.synchronize()
     def moved_rows():
-        # rows the pass just run moved: its kept rows at or past row B (each moves to a freed slot
-        # below B). From its scores (row order before the moves): the B-th largest score T per
-        # unit; rows above T are kept, rows equal to T lowest row first up to B in all.
-        sc = plan_scores.view(U, C)
-        T = torch.topk(sc, B, dim=1).values[:, -1:]
-        gt, eq = sc > T, sc == T
-        need = B - gt.sum(dim=1)
-        ties_kept = torch.minimum(need, eq.sum(dim=1))
-        return (gt[:, B:].sum(dim=1) + (ties_kept - eq[:, :B].sum(dim=1)).clamp(min=0)).sum()
+        return count_moved_rows(torch, plan_scores.view(U, C), B)
 
     evs, moves = [], []
     for _ in range(steps):
