@@ -80,7 +80,8 @@ class Cache:
     def check_pass(self, B, label, max_rows=None):
         """Run one in-place pass and check it; then adopt the expected arrangement."""
         scores, kept_cnt, K, V, pos = self.run(B, max_rows)
-        worst, self.mism = 0.0, 0
+        worst, self.mism, self.moved = 0.0, 0, 0
+        self.scores = scores
         for u in range(len(self.lengths)):
             a, b = self.row_off[u], self.row_off[u + 1]
             n = b - a
@@ -101,6 +102,7 @@ class Cache:
             assert np.array_equal(pos[a + m:b], self.pos[a + m:b]), (label, u)
             moved = int(np.sum(src != np.arange(m)))
             assert moved <= min(m, n - m)
+            self.moved += moved
         self.K, self.V, self.pos = K, V, pos
         return worst
 
@@ -149,7 +151,11 @@ def test_inplace_steady_state(dtype, max_rows):
         c = Cache(wl, np.concatenate(Kn), np.concatenate(Vn), np.concatenate(Pn), [B + chunk] * U, [t] * U, centers)
         say(f"case in-place steady state {dtype}: pass {k} (positions sparse: {np.unique(np.diff(np.sort(c.pos[:B]))).size} gaps)")
         err = c.check_pass(B, f"pass {k}", max_rows)
-        say(f"   worst score error {err:.3g}")
+        say(f"   worst score error {err:.3g}, {c.moved} rows moved")
+        # the bench's count of moved rows, from the scores alone, agrees with the moves made
+        import bench
+        sc = torch.from_numpy(c.scores.reshape(U, B + chunk).copy())
+        assert int(bench.count_moved_rows(torch, sc, B).item()) == c.moved, (k, c.moved)
         say(f"[margin] in-place steady state ({dtype}, 4 units, {B} + {chunk} rows, pass {k}"
             f"{', max_rows ' + str(max_rows) if max_rows else ''}) | {err:.3g} | {c.mism} | {U}")
 
